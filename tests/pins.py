@@ -1,0 +1,280 @@
+"""Independent checks that pin the oracle to something other than itself.
+
+Each check derives the expected result a different way from the oracle:
+closed forms (bincount, prefix sums), library routines (a stable argsort,
+nonzero of the token x rank hit matrix), O(T^2) brute force, and an exact
+rational replay of the fp32 fused-multiply-add chain.  Every function raises
+AssertionError on a mismatch; test_oracle_mutants.py plants mistakes in a
+copy of the oracle and requires that some check here fails.
+"""
+
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# plan
+# --------------------------------------------------------------------------
+
+def hit_matrix(idx: np.ndarray, E: int, R: int) -> np.ndarray:
+    T = idx.shape[0]
+    hit = np.zeros((T, R), dtype=bool)
+    if T:
+        hit[np.repeat(np.arange(T), idx.shape[1]), (idx // (E // R)).ravel()] = True
+    return hit
+
+
+def check_counts(p: dict, idx: np.ndarray, E: int, R: int):
+    """Closed forms: histogram, distinct ranks per token, prefix sums."""
+    T, k = idx.shape
+    np.testing.assert_array_equal(p["expert_count"], np.bincount(idx.ravel(), minlength=E))
+    hit = hit_matrix(idx, E, R)
+    np.testing.assert_array_equal(p["rank_count"], hit.sum(axis=0))
+    np.testing.assert_array_equal(p["expert_offset"], np.concatenate([[0], np.cumsum(p["expert_count"])]))
+    np.testing.assert_array_equal(p["rank_offset"], np.concatenate([[0], np.cumsum(p["rank_count"])]))
+    N = int(hit.sum())
+    assert p["N"] == N
+    assert int(p["expert_count"].sum()) == T * k
+    assert N <= T * min(k, R)
+    Epr = E // R
+    for r in range(R):
+        assert p["rank_count"][r] <= min(T, int(p["expert_count"][r * Epr:(r + 1) * Epr].sum()))
+
+
+def check_expert_side_argsort(p: dict, idx: np.ndarray, E: int, R: int):
+    """Expert-major placement == a stable sort of the flattened top-k ids."""
+    T, k = idx.shape
+    perm = np.argsort(idx.ravel(), kind="stable")          # expert row q holds pair perm[q]
+    cr = p["comb_row"].ravel()
+    np.testing.assert_array_equal(cr[perm], np.arange(T * k))
+    if T * k:
+        tok_of_q = perm // k
+        np.testing.assert_array_equal(p["send_token"][p["fan_src"]], tok_of_q)
+        rank_of_q = idx.ravel()[perm] // (E // R)
+        ro = p["rank_offset"]
+        p_of_q = p["fan_src"]
+        assert np.all((p_of_q >= ro[rank_of_q]) & (p_of_q < ro[rank_of_q + 1]))
+
+
+def check_rank_side_nonzero(p: dict, idx: np.ndarray, E: int, R: int):
+    """Rank-major placement == nonzero() of the hit matrix read rank-major."""
+    T, k = idx.shape
+    hit = hit_matrix(idx, E, R)
+    r_list, t_list = np.nonzero(hit.T)
+    np.testing.assert_array_equal(p["send_token"], t_list)
+    KR = min(k, R)
+    expect = np.full((T, KR), -1, np.int32)
+    order = np.argsort(t_list, kind="stable")              # rows grouped by token, rank ascending
+    ts = t_list[order]
+    slot = np.arange(len(ts)) - np.searchsorted(ts, ts, side="left")
+    expect[ts, slot] = order
+    np.testing.assert_array_equal(p["tok_rank_row"], expect)
+
+
+def check_fan_dst(p: dict, idx: np.ndarray, E: int, R: int):
+    """The receiver map lists, per rank row, exactly the expert rows whose source it is."""
+    T, k = idx.shape
+    D = min(k, E // R)
+    N = p["N"]
+    expect = np.full((N, D), -1, np.int32)
+    order = np.argsort(p["fan_src"], kind="stable")          # expert rows grouped by source, q ascending
+    fs = p["fan_src"][order]
+    j = np.arange(len(fs)) - np.searchsorted(fs, fs, side="left")
+    assert np.all(j < D), "a rank row feeds more expert rows than experts per rank"
+    expect[fs, j] = order
+    np.testing.assert_array_equal(p["fan_dst"], expect)
+
+
+def check_segments(p: dict, E: int, R: int):
+    Epr = E // R
+    rs = np.stack([np.arange(R), -np.ones(R, int), p["rank_offset"][:-1], p["rank_count"]], axis=1)
+    es = np.stack([np.arange(E) // Epr, np.arange(E), p["expert_offset"][:-1], p["expert_count"]], axis=1)
+    np.testing.assert_array_equal(p["rank_segs"], rs)
+    np.testing.assert_array_equal(p["expert_segs"], es)
+
+
+def check_brute_force(p: dict, idx: np.ndarray, E: int, R: int):
+    """O(T^2) definition of every row position, for tiny T."""
+    T, k = idx.shape
+    Epr = E // R
+    ranks = [sorted({int(e) // Epr for e in idx[t]}) for t in range(T)]
+    for t in range(T):
+        for i, r in enumerate(ranks[t]):
+            before = sum(1 for u in range(t) if r in ranks[u])
+            assert p["tok_rank_row"][t, i] == p["rank_offset"][r] + before
+        for j in range(k):
+            e = int(idx[t, j])
+            before = sum(1 for u in range(t) if e in set(idx[u].tolist()))
+            q = p["expert_offset"][e] + before
+            assert p["comb_row"][t, j] == q
+            assert p["fan_src"][q] == p["tok_rank_row"][t, ranks[t].index(e // Epr)]
+
+
+def check_plan_all(p: dict, idx: np.ndarray, E: int, R: int, brute: bool = False):
+    check_counts(p, idx, E, R)
+    check_expert_side_argsort(p, idx, E, R)
+    check_rank_side_nonzero(p, idx, E, R)
+    check_fan_dst(p, idx, E, R)
+    check_segments(p, E, R)
+    if brute:
+        check_brute_force(p, idx, E, R)
+
+
+# --------------------------------------------------------------------------
+# dispatch
+# --------------------------------------------------------------------------
+
+def check_dispatch(p: dict, idx: np.ndarray, x: np.ndarray, xr: np.ndarray, xe: np.ndarray):
+    """Every rank row is its token's x row; every expert row is its token's x
+    row (the token of expert row q is perm[q] // k for the stable sort perm)."""
+    T, k = idx.shape
+    np.testing.assert_array_equal(xr, x[p["send_token"]])
+    perm = np.argsort(idx.ravel(), kind="stable")
+    np.testing.assert_array_equal(xe, x[perm // k] if T * k else xe)
+
+
+# --------------------------------------------------------------------------
+# combine: exact replay of the fp32 chain with rationals
+# --------------------------------------------------------------------------
+
+def _round_fraction(x: Fraction, prec: int, emin: int, emax: int) -> float:
+    """Round a rational to the nearest value of a binary format with `prec`
+    significand bits (ties to even), gradual underflow below 2**emin and
+    overflow to infinity above the largest finite value."""
+    if x == 0:
+        return 0.0
+    sign = -1.0 if x < 0 else 1.0
+    a = -x if x < 0 else x
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, emin)
+    quantum = Fraction(2) ** (e - prec + 1)
+    m = a / quantum
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    val = n * quantum
+    if val >= Fraction(2) ** (emax + 1):
+        return sign * float("inf")
+    return sign * float(val)
+
+
+def f32_fma_exact(a: float, b: float, c: float) -> float:
+    """fp32 fused multiply-add: the exact a*b+c rounded once to binary32."""
+    return _round_fraction(Fraction(a) * Fraction(b) + Fraction(c), 24, -126, 127)
+
+
+def bf16_bits_of_exact(v: float) -> int:
+    """bf16 (round to nearest even) of an fp32 value, as bits."""
+    if v != v:
+        raise ValueError("nan")
+    if v in (float("inf"), float("-inf")):
+        r = v
+    else:
+        r = _round_fraction(Fraction(v), 8, -126, 127)
+    bits = int(np.array([r], dtype=np.float32).view(np.uint32)[0]) >> 16
+    return bits
+
+
+def combine_exact(comb_row: np.ndarray, ye_bits: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """out[t,h] for the chain acc=+0; acc=fma(w[t,j], ye[q,h], acc), j ascending."""
+    T, k = comb_row.shape
+    H = ye_bits.shape[1]
+    yf = (ye_bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    out = np.zeros((T, H), np.uint16)
+    for t in range(T):
+        for h in range(H):
+            acc = 0.0
+            for j in range(k):
+                acc = f32_fma_exact(float(w[t, j]), float(yf[comb_row[t, j], h]), acc)
+            out[t, h] = bf16_bits_of_exact(acc)
+    return out
+
+
+def bf16_ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """|ord(a) - ord(b)| on bf16 bit patterns; +0 and -0 are equal."""
+    def ordkey(u):
+        u = u.astype(np.int64)
+        return np.where(u & 0x8000, 0x8000 - (u & 0x7FFF), 0x8000 + u)
+    return np.abs(ordkey(a) - ordkey(b))
+
+
+# --------------------------------------------------------------------------
+# the whole battery, as one function (used on planted-mistake oracle copies)
+# --------------------------------------------------------------------------
+
+def tie_rows():
+    """Two bf16 rows whose sum (gates 1, 1) lands exactly half-way between
+    two bf16 values in every column: even and odd neighbours, both signs."""
+    r0 = np.array([1.0, 1.0 + 2.0 ** -7, 2.0, -1.0, -(1.0 + 2.0 ** -7), 0.5, 3.0, 1.0], np.float32)
+    r1 = np.array([2.0 ** -8, 2.0 ** -8, 2.0 ** -7, -(2.0 ** -8), -(2.0 ** -8), 2.0 ** -9, 2.0 ** -7, 0.0], np.float32)
+    return r0, r1
+
+
+def edge_combine_case():
+    """Hand-built rows where the order, the fusing and the gate index of the
+    fp32 chain each change the bf16 result (the rows hold bf16 values):
+      token 0: y = [1, -1, 2^-30], w = [1, 1, 1]: ascending gives 2^-30, any
+               other order loses the small term (cancellation);
+      token 1: w = [-1, 1+2^-23], y = [1+2^-7, 1+2^-7]: the fused step keeps
+               the product's low bits (2^-23 + 2^-30), an unfused one gives 2^-23.
+    """
+    import synth
+    rows = np.array([[1.0] * 8, [-1.0] * 8, [2.0 ** -30] * 8, [1.0 + 2.0 ** -7] * 8], np.float32)
+    ye = synth.f32_to_bf16_bits(rows)
+    comb_row = np.array([[0, 1, 2], [3, 3, 3]], np.int32)
+    w = np.array([[1.0, 1.0, 1.0], [-1.0, 1.0 + 2.0 ** -23, 0.0]], np.float32)
+    return comb_row, ye, w
+
+
+def run_battery(orc) -> None:
+    import json
+    import os
+    import synth
+    here = os.path.dirname(os.path.abspath(__file__))
+    g = json.load(open(os.path.join(here, "golden", "fig3_two_tokens.json")))
+    d, ex = g["dims"], g["expected"]
+    idx = np.array(g["topk_idx"], np.int32)
+    rc, p = orc.plan(idx, d["H"], d["E"], d["R"])
+    assert rc == 0
+    for key in ("expert_count", "rank_count", "send_token", "tok_rank_row", "fan_src", "fan_dst", "comb_row"):
+        np.testing.assert_array_equal(p[key], np.array(ex[key]))
+    for (T, E, k, R) in ((17, 8, 3, 4), (40, 12, 3, 2), (23, 16, 4, 16), (9, 8, 8, 2)):
+        rng = np.random.default_rng(T * 31 + E)
+        idx, _ = synth.random_routing(rng, T, E, k)
+        rc, p = orc.plan(idx, 16, E, R)
+        assert rc == 0
+        check_plan_all(p, idx, E, R, brute=True)
+        x = synth.random_bf16(rng, (T, 16))
+        xr, xe = orc.dispatch(p, x, E, k, R)
+        check_dispatch(p, idx, x, xr, xe)
+    for cfg_id in (0, 1):
+        cfg = synth.CONFIGS[cfg_id]
+        inp = synth.make_inputs(cfg, 0)
+        rc, p = orc.plan(inp["topk_idx"], cfg.H, cfg.E, cfg.R)
+        check_plan_all(p, inp["topk_idx"], cfg.E, cfg.R)
+        xr, xe = orc.dispatch(p, inp["x"], cfg.E, cfg.k, cfg.R)
+        out = orc.combine(p["comb_row"], xe, inp["topk_w"], cfg.E, cfg.R)
+        np.testing.assert_array_equal(out, np.where(inp["x"] == 0x8000, 0, inp["x"]).astype(np.uint16))
+    for seed in range(3):
+        rng = np.random.default_rng(100 + seed)
+        T, H, k, Q = 6, 16, 5, 40
+        ye = synth.f32_to_bf16_bits((rng.standard_normal((Q, H)) * 2.0 ** rng.integers(-12, 13, size=(Q, H))).astype(np.float32))
+        w = (rng.standard_normal((T, k)) * 2.0 ** rng.integers(-6, 7, size=(T, k))).astype(np.float32)
+        comb_row = np.stack([rng.choice(Q, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+        np.testing.assert_array_equal(orc.combine(comb_row, ye, w, 8, 1), combine_exact(comb_row, ye, w))
+    comb_row, ye, w = edge_combine_case()
+    np.testing.assert_array_equal(orc.combine(comb_row, ye, w, 4, 1), combine_exact(comb_row, ye, w))
+    r0, r1 = tie_rows()
+    tiny = np.array([2.0 ** -130, -2.0 ** -131, 2.0 ** -133, 3 * 2.0 ** -128] * 2, np.float32)
+    ye = synth.f32_to_bf16_bits(np.stack([r0, r1, tiny, tiny * 5]))
+    comb_row = np.array([[0, 1], [2, 3]], np.int32)
+    w = np.array([[1.0, 1.0], [0.5, 0.25]], np.float32)
+    np.testing.assert_array_equal(orc.combine(comb_row, ye, w, 4, 1), combine_exact(comb_row, ye, w))

@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE token shuffle on one MI355X.
+
+One step = the whole hot path on one batch: plan (count, scan, place),
+dispatch send (x -> rank-major xr), dispatch fan-out (xr -> expert-major
+xe), combine (identity expert: ye = xe -> out).  Inputs are seeded
+synthetic data already resident in HBM when the timed region starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+Prints one JSON line.  `value` is algorithmic bytes per step / wall time per
+step (GB/s, plan included); algorithmic bytes are what the method must
+move: 2H(T+N) + 2H(N+Tk) + 2H(Tk+T) + 4(N+Tk) + 8Tk, with N the number of
+deduplicated (token, rank) rows.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
+METRIC = "dispatch+combine effective HBM GB/s (fraction of peak) and tokens/s, 1 GPU"
+KERNEL_SRC = os.path.join(ROOT, "moe_expert_token_amd", "csrc", "shuffle_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(T, H, k, N):
+    row = 2 * H
+    send = row * (T + N) + 4 * N
+    fanout = row * (N + T * k) + 4 * T * k
+    combine = row * (T * k + T) + 8 * T * k
+    return {"send": send, "fanout": fanout, "combine": combine, "total": send + fanout + combine}
+
+
+def bf16_order(u):
+    """Monotone integer key of bf16 bit patterns (+0 and -0 equal)."""
+    import numpy as np
+    u = u.astype(np.int64)
+    return np.where(u & 0x8000, 0x8000 - (u & 0x7FFF), 0x8000 + u)
+
+
+def source_digest() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel: str, per_launch_alg: float):
+    """HBM traffic from the committed rocprofv3 counter summary, only while the
+    kernel source still matches the one that was profiled."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    if rec.get("kernel_src_sha256_16") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload id (0..4); default: DeepSeek-V3-like")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0, help="CPU-oracle timing budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the shuffle runs its expert-parallel ranks as logical "
+              f"partitions of one GPU's HBM (asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_expert_token_amd as ms
+    import synth
+
+    if not os.path.exists(ms.LIB_PATH):
+        from moe_expert_token_amd import build as hip_build
+        hip_build.build()
+    ms.load()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+
+    cfg = synth.CONFIGS[args.config]
+    T, H, E, k, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.R
+    KR = min(k, R)
+    log(f"[bench] workload {cfg.name}: generating inputs")
+    inp = synth.make_inputs(cfg, args.seed)
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev)
+    idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    w = torch.from_numpy(inp["topk_w"]).to(dev)
+    dims = ms.dims_of(T, H, E, k, R)
+    ws = torch.empty(ms.moe_shuffle_workspace_size(dims), dtype=torch.uint8, device=dev)
+    xr = torch.empty((T * KR, H), dtype=torch.int16, device=dev)   # no host sync: sized by T*min(k,R)
+    xe = torch.empty((T * k, H), dtype=torch.int16, device=dev)
+    out = torch.empty((T, H), dtype=torch.int16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        plan = ms.moe_shuffle_plan(dims, idx, ws)
+        if ev is not None:
+            ev[1].record()
+        ms.moe_shuffle_dispatch_send(plan, x, xr)
+        if ev is not None:
+            ev[2].record()
+        ms.moe_shuffle_dispatch_fanout(plan, xr, xe)
+        if ev is not None:
+            ev[3].record()
+        ms.moe_shuffle_combine(plan, xe, w, out)      # identity expert: ye is xe
+        if ev is not None:
+            ev[4].record()
+        return plan
+
+    for _ in range(args.warmup):
+        ms.moe_shuffle_plan_destroy(step())
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    plans = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        plans.append(step(events[i]))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    last_plan = plans[-1]
+    for p in plans[:-1]:
+        ms.moe_shuffle_plan_destroy(p)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    names = ("plan", "send", "fanout", "combine")
+    us = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]) * 1e3)
+          for j, n in enumerate(names)}
+    info = ms.moe_shuffle_plan_query(last_plan)
+    N = info["N"]
+    B = algorithmic_bytes(T, H, k, N)
+    log(f"[bench] {ms_per_step:.3f} ms/step; kernels (us): " + ", ".join(f"{n} {us[n]:.1f}" for n in names))
+
+    # copy ceiling: the runtime's device-to-device copy of a buffer as big as xe
+    nbytes = min(T * k * H * 2, 2 << 30)
+    a = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        b.copy_(a)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del a, b
+
+    parity = None
+    if not args.no_parity:
+        import oracle
+        orc = oracle.get()
+        rc, o = orc.plan(inp["topk_idx"], H, E, R)
+        v = ms.plan_array_views(last_plan, N)
+        plan_ok = rc == 0 and o["N"] == N and all(
+            np.array_equal(v[key].cpu().numpy(), o[key])
+            for key in ("send_token", "tok_rank_row", "fan_src", "fan_dst", "comb_row", "expert_offset",
+                        "rank_offset", "rank_segs", "expert_segs"))
+        oxr, oxe = orc.dispatch(o, inp["x"], E, k, R)
+        xr_ok = np.array_equal(xr[:N].cpu().numpy().view(np.uint16), oxr)
+        xe_ok = np.array_equal(xe.cpu().numpy().view(np.uint16), oxe)
+        oout = orc.combine(o["comb_row"], oxe, inp["topk_w"], E, R)
+        got = out.cpu().numpy().view(np.uint16)
+        parity = {"plan_bitexact": bool(plan_ok), "xr_bitexact": bool(xr_ok), "xe_bitexact": bool(xe_ok),
+                  "out_max_ulp": int(np.abs(bf16_order(got) - bf16_order(oout)).max()),
+                  "out_bitexact": bool(np.array_equal(got, oout))}
+        log(f"[bench] parity vs oracle: {parity}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.get()
+        reps, tcpu = 0, 0.0
+        while reps == 0 or (tcpu < args.cpu_budget_s and reps < 20):
+            s0 = time.perf_counter()
+            rc, o = orc.plan(inp["topk_idx"], H, E, R)
+            oxr, oxe = orc.dispatch(o, inp["x"], E, k, R)
+            orc.combine(o["comb_row"], oxe, inp["topk_w"], E, R)
+            tcpu += time.perf_counter() - s0
+            reps += 1
+        t_rep = tcpu / reps
+        cpu = {"value": round(B["total"] / t_rep / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"the full {cfg.name} workload, {reps} pass(es) of plan+dispatch+combine, "
+                         f"single-threaded C oracle, {t_rep:.2f} s per pass",
+               "tokens_per_s": round(T / t_rep, 1), "host_cpus": os.cpu_count()}
+        log(f"[bench] cpu oracle: {cpu}")
+
+    # dominant kernel by algorithmic bytes: the receiver fan-out
+    dom = max(("send", "fanout", "combine"), key=lambda n: B[n])
+    achieved = B[dom] / (us[dom] * 1e-6) / 1e9
+    traffic = load_traffic(cfg.name, dom, B[dom])
+    dc_us = us["send"] + us["fanout"] + us["combine"]
+    value = B["total"] / (ms_per_step * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "H": H, "E": E, "k": k, "R": R, "N": N,
+                   "parallelism": f"ep{R}-logical-on-1gpu"},
+        "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "dispatch_combine_GBps": round((B["send"] + B["fanout"] + B["combine"]) / (dc_us * 1e-6) / 1e9, 1),
+        "dispatch_combine_frac_of_peak": round((B["total"]) / (dc_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "kernel_us": {n: round(us[n], 2) for n in names},
+        "algorithmic_bytes": B,
+        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "accumulate": "fp32",
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "alg_bytes_per_launch": B[dom], "avg_launch_us": round(us[dom], 2)},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "kernel_src_sha256_16": source_digest(),
+    }
+    ms.moe_shuffle_plan_destroy(last_plan)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

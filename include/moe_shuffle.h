@@ -1,0 +1,195 @@
+/*
+ * moe_shuffle.h -- C ABI of the MoE token shuffle for AMD MI355X (gfx950).
+ *
+ * The shuffle moves token activations to experts and back on one GPU, with
+ * expert-parallel ranks as logical partitions of one HBM buffer:
+ *
+ *   plan      routing -> counts, offsets, row maps and segment descriptors
+ *   dispatch  token-major x -> rank-major xr (one row per (token, rank) pair)
+ *             -> expert-major xe (receiver fan-out, read from xr)
+ *   combine   expert outputs ye -> gate-weighted top-k sum in token order
+ *
+ * Sources (cited by page and section):
+ *  - FUSCO abstract ("FUSCO: High-Performance Distributed Data Shuffling via
+ *    Transformation-Communication Fusion"): the experts need an expert-major
+ *    layout, the exchange a device-major one; the layout is captured once
+ *    and the reshaping is done on the way; light-weight planning removes
+ *    redundant sends.
+ *  - FUSCO press summary, Groups 2-3: the interface is a set of logical
+ *    segments that say exactly where each row is read and placed, with no
+ *    staging buffer and no rearrangement afterwards.
+ *  - DySHARP write-up ("Accelerating MoE with Dynamic In-Switch Computing on
+ *    Multi-GPUs"), section 2 / Fig. 1 (dispatch and combine, and the
+ *    duplicate payloads they carry) and section 5 / Fig. 5, Fig. 9 (a token
+ *    keeps one logical index plus a target list; each destination keeps its
+ *    own map from that index to its local rows).
+ *
+ * Conventions for every call:
+ *  - Dimensions: T tokens, H hidden size, E experts, k top-k, R ranks,
+ *    Epr = E / R experts per rank; expert e lives on rank e / Epr.
+ *    KR = min(k, R) (ranks one token can reach), D = min(k, Epr) (experts of
+ *    one rank one token can use).  N = number of deduplicated (token, rank)
+ *    rows, known on the device after plan (host: moe_shuffle_plan_query).
+ *  - Activations are bf16, passed as raw 16-bit patterns; rows are
+ *    contiguous and row-major, H elements each.  Gates are fp32 [T, k].
+ *    topk_idx is int32 [T, k]; its k ids must be distinct and in [0, E).
+ *  - Every pointer argument named as device memory is caller-owned device
+ *    memory (e.g. a torch tensor).  The library allocates no device memory.
+ *  - H % 8 == 0 and all activation pointers 16-byte aligned (rows move as
+ *    16-byte vectors); the workspace must be 256-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    All calls are asynchronous and stream-ordered except
+ *    moe_shuffle_plan_query, which synchronises the stream.
+ *  - Every function returns an int status (MOE_SHUFFLE_OK or a negative
+ *    code below); nothing is thrown across the ABI.  A failing call writes
+ *    no output.
+ *  - Implementation limits: E + R <= 1024, k <= 64, T * k < 2^31
+ *    (otherwise MOE_SHUFFLE_E_OVERFLOW).
+ */
+#ifndef MOE_SHUFFLE_H
+#define MOE_SHUFFLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    MOE_SHUFFLE_OK = 0,
+    MOE_SHUFFLE_E_INVALID_ARG = -1, /* null pointer, dims <= 0 (T may be 0), k > E, E % R != 0,
+                                       overlapping buffers, too small xr */
+    MOE_SHUFFLE_E_ALIGN = -2,       /* H % 8 != 0, or a pointer not 16 B (workspace: 256 B) aligned */
+    MOE_SHUFFLE_E_WORKSPACE = -3,   /* workspace smaller than moe_shuffle_workspace_size() */
+    MOE_SHUFFLE_E_BAD_INDEX = -4,   /* a top-k id out of [0, E) or repeated within a token;
+                                       detected on the device, reported by plan_query */
+    MOE_SHUFFLE_E_HIP = -5,         /* a HIP launch or runtime call failed (see
+                                       moe_shuffle_last_hip_error) */
+    MOE_SHUFFLE_E_OVERFLOW = -6     /* sizes beyond the implementation limits */
+};
+
+/* Opaque host-side plan handle: the dims plus the workspace it lives in. */
+typedef struct moe_shuffle_plan_s* moe_shuffle_plan_t;
+
+typedef struct {
+    int32_t num_tokens;  /* T >= 0 */
+    int32_t hidden;      /* H > 0, multiple of 8 */
+    int32_t num_experts; /* E > 0 */
+    int32_t top_k;       /* 0 < k <= E */
+    int32_t num_ranks;   /* R > 0, E % R == 0 */
+} moe_shuffle_dims;
+
+/* A logical segment: rows [row_offset, row_offset + row_count) of the
+ * rank-major buffer (expert == -1) or of the expert-major buffer. */
+typedef struct {
+    int32_t rank, expert, row_offset, row_count;
+} moe_segment;
+
+typedef struct {
+    int32_t n_rank_rows;   /* N */
+    int32_t n_expert_rows; /* T * k */
+    int32_t status;        /* MOE_SHUFFLE_OK or MOE_SHUFFLE_E_BAD_INDEX */
+    int32_t max_rank_rows; /* T * KR, the bound usable without a query */
+} moe_shuffle_plan_info;
+
+/* Device pointers into the workspace, valid after the plan's kernels ran. */
+typedef struct {
+    int32_t* expert_count;  /* [E]   routed (token, expert) pairs per expert */
+    int32_t* expert_offset; /* [E+1] exclusive prefix sum of expert_count */
+    int32_t* rank_count;    /* [R]   distinct tokens per rank */
+    int32_t* rank_offset;   /* [R+1] exclusive prefix sum of rank_count; [R] = N */
+    int32_t* send_token;    /* [N]   rank row p -> its token */
+    int32_t* tok_rank_row;  /* [T][KR] token -> its rank rows, ranks ascending, -1 padded */
+    int32_t* fan_src;       /* [T*k] expert row q -> the rank row it is copied from */
+    int32_t* fan_dst;       /* [N][D] rank row -> the expert rows it feeds, ascending, -1 padded */
+    int32_t* comb_row;      /* [T][k] (token, slot) -> its expert row */
+    moe_segment* rank_segs;   /* [R] */
+    moe_segment* expert_segs; /* [E] */
+    int32_t* status;        /* [1] */
+    int32_t* n_rank_rows;   /* [1] N */
+    int32_t tok_rank_width; /* KR */
+    int32_t fan_dst_width;  /* D */
+} moe_shuffle_plan_arrays;
+
+/* Bytes of device workspace a plan with these dims needs (host only, no
+ * device work).  Errors: INVALID_ARG, ALIGN, OVERFLOW for bad dims. */
+int moe_shuffle_workspace_size(const moe_shuffle_dims* dims, size_t* bytes);
+
+/*
+ * Plan the routing (FUSCO abstract: the planner; press summary, Group 3:
+ * the logical segments).  Counts experts and distinct (token, rank) pairs
+ * per token tile, scans them into offsets, and places every row in
+ * ascending token order inside its segment.
+ *   topk_idx   device int32 [T, k]; must stay alive until the plan's
+ *              kernels have run on `stream`.
+ *   workspace  device, >= moe_shuffle_workspace_size() bytes, 256 B
+ *              aligned; holds every plan array; must stay alive and
+ *              unmodified while the plan is used.
+ *   plan       out: a new host handle (free with moe_shuffle_plan_destroy).
+ * Bad top-k ids are found on the device: the status word is set, the
+ * place step and every later dispatch/combine on this plan write nothing,
+ * and moe_shuffle_plan_query returns MOE_SHUFFLE_E_BAD_INDEX.
+ */
+int moe_shuffle_plan(const moe_shuffle_dims* dims, const int32_t* topk_idx, void* workspace,
+                     size_t workspace_bytes, void* stream, moe_shuffle_plan_t* plan);
+
+/*
+ * Dispatch = send, then fan-out (FUSCO abstract: token-major to
+ * device-major without a separate rearrangement pass; DySHARP section 2:
+ * a token bound for a rank is sent there once).
+ *   x        device bf16 [T, H], read only.
+ *   xr       device bf16 [xr_rows, H]; rows [0, N) are written.  xr_rows
+ *            must be >= T*KR, or >= N once moe_shuffle_plan_query has run.
+ *   xe       device bf16 [T*k, H]; every row is written.
+ * x, xr and xe must not overlap.
+ */
+int moe_shuffle_dispatch(moe_shuffle_plan_t plan, const void* x, void* xr, int64_t xr_rows,
+                         void* xe, void* stream);
+
+/* The send half alone: xr[p] = x[send_token[p]] for p < N.  Each x row is
+ * read once and written to its <= KR rank rows. */
+int moe_shuffle_dispatch_send(moe_shuffle_plan_t plan, const void* x, void* xr, int64_t xr_rows,
+                              void* stream);
+
+/* The receiver half alone (DySHARP section 5: each destination maps the
+ * arriving row to its own local rows): xe[q] = xr[fan_src[q]] for q < T*k,
+ * done by reading each rank row once and writing its <= D expert rows. */
+int moe_shuffle_dispatch_fanout(moe_shuffle_plan_t plan, const void* xr, int64_t xr_rows, void* xe,
+                                void* stream);
+
+/*
+ * Combine (DySHARP section 2 / Fig. 1: the expert results of a token are
+ * summed back into its row):
+ *   out[t, h] = bf16_rne( acc ),  acc = +0.0f, then for j = 0 .. k-1:
+ *               acc = fmaf(topk_w[t, j], float(ye[comb_row[t, j], h]), acc)
+ *   ye      device bf16 [T*k, H] (expert-major, as dispatch laid out xe; it
+ *           may be the xe buffer itself).
+ *   topk_w  device fp32 [T, k].
+ *   out     device bf16 [T, H]; must not overlap ye.
+ */
+int moe_shuffle_combine(moe_shuffle_plan_t plan, const void* ye, const float* topk_w, void* out,
+                        void* stream);
+
+/* Synchronises `stream`, reads N and the status word back to the host.
+ * Returns the plan's status (MOE_SHUFFLE_OK or MOE_SHUFFLE_E_BAD_INDEX). */
+int moe_shuffle_plan_query(moe_shuffle_plan_t plan, void* stream, moe_shuffle_plan_info* info);
+
+/* Device pointers of the plan arrays (no device work, no sync). */
+int moe_shuffle_plan_arrays_get(moe_shuffle_plan_t plan, moe_shuffle_plan_arrays* arrays);
+
+/* Frees the host handle (not the workspace).  NULL is ignored. */
+void moe_shuffle_plan_destroy(moe_shuffle_plan_t plan);
+
+/* Static text for a status code. */
+const char* moe_shuffle_strerror(int code);
+
+/* The hipError_t of the calling thread's last MOE_SHUFFLE_E_HIP. */
+int moe_shuffle_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_SHUFFLE_H */

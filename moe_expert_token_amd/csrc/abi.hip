@@ -1,0 +1,322 @@
+// abi.hip -- the extern "C" boundary: argument checks, workspace layout,
+// launches and error mapping.  Everything that touches data runs in the
+// kernels of shuffle_kernels.hip; this file only validates and launches.
+#include <hip/hip_runtime.h>
+
+#include <stdlib.h>
+#include <string.h>
+
+#include "internal.h"
+#include "moe_shuffle.h"
+
+struct moe_shuffle_plan_s {
+    moe_shuffle_dims dims;
+    ms::Layout L;
+    char* ws;
+    int64_t n_known;  // N after moe_shuffle_plan_query, else -1
+};
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e)
+{
+    g_last_hip_error = (int)e;
+    return MOE_SHUFFLE_E_HIP;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_dims(const moe_shuffle_dims* d)
+{
+    if (!d) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (d->num_tokens < 0 || d->hidden <= 0 || d->num_experts <= 0 || d->top_k <= 0 || d->num_ranks <= 0)
+        return MOE_SHUFFLE_E_INVALID_ARG;
+    if (d->top_k > d->num_experts || d->num_experts % d->num_ranks != 0) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (d->hidden % 8 != 0) return MOE_SHUFFLE_E_ALIGN;
+    if ((int64_t)d->num_tokens * d->top_k >= ((int64_t)1 << 31)) return MOE_SHUFFLE_E_OVERFLOW;
+    if (d->top_k > ms::kMaxTopK || d->num_experts + d->num_ranks > ms::kMaxCols) return MOE_SHUFFLE_E_OVERFLOW;
+    return MOE_SHUFFLE_OK;
+}
+
+bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn)
+{
+    if (an == 0 || bn == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+int check_plan(const moe_shuffle_plan_s* p)
+{
+    return (p && p->ws) ? MOE_SHUFFLE_OK : MOE_SHUFFLE_E_INVALID_ARG;
+}
+
+template <class T>
+T* at(const moe_shuffle_plan_s* p, size_t off) { return (T*)(p->ws + off); }
+
+int64_t rank_rows_needed(const moe_shuffle_plan_s* p)
+{
+    return p->n_known >= 0 ? p->n_known : (int64_t)p->L.T * p->L.KR;
+}
+
+}  // namespace
+
+namespace ms {
+
+void make_layout(const moe_shuffle_dims& d, Layout& L)
+{
+    L.T = d.num_tokens; L.H = d.hidden; L.E = d.num_experts; L.k = d.top_k; L.R = d.num_ranks;
+    L.Epr = L.E / L.R;
+    L.KR = L.k < L.R ? L.k : L.R;
+    L.D = L.k < L.Epr ? L.k : L.Epr;
+    L.C = L.E + L.R;
+    L.ntiles = L.T > 0 ? (L.T + kPlanTile - 1) / kPlanTile : 1;
+    const size_t T = (size_t)L.T, k = (size_t)L.k, KR = (size_t)L.KR, D = (size_t)L.D, i4 = sizeof(int32_t);
+    size_t o = 0;
+    auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
+    L.status = take(i4);
+    L.n_rank_rows = take(i4);
+    L.expert_count = take(i4 * L.E);
+    L.expert_offset = take(i4 * (L.E + 1));
+    L.rank_count = take(i4 * L.R);
+    L.rank_offset = take(i4 * (L.R + 1));
+    L.send_token = take(i4 * T * KR);
+    L.tok_rank_row = take(i4 * T * KR);
+    L.fan_src = take(i4 * T * k);
+    L.fan_dst = take(i4 * T * KR * D);
+    L.comb_row = take(i4 * T * k);
+    L.rank_segs = take(4 * i4 * L.R);
+    L.expert_segs = take(4 * i4 * L.E);
+    L.tile_hist = take(i4 * (size_t)(L.C + 1) * L.ntiles);
+    L.tile_base = take(i4 * (size_t)L.C * L.ntiles);
+    L.col_total = take(i4 * L.C);
+    L.total = o;
+}
+
+}  // namespace ms
+
+extern "C" {
+
+int moe_shuffle_workspace_size(const moe_shuffle_dims* dims, size_t* bytes)
+{
+    const int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!bytes) return MOE_SHUFFLE_E_INVALID_ARG;
+    ms::Layout L;
+    ms::make_layout(*dims, L);
+    *bytes = L.total;
+    return MOE_SHUFFLE_OK;
+}
+
+int moe_shuffle_plan(const moe_shuffle_dims* dims, const int32_t* topk_idx, void* workspace, size_t workspace_bytes,
+                     void* stream, moe_shuffle_plan_t* plan)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!plan || !workspace || (dims->num_tokens > 0 && !topk_idx)) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (misaligned(workspace, 256) || misaligned(topk_idx, 4)) return MOE_SHUFFLE_E_ALIGN;
+    ms::Layout L;
+    ms::make_layout(*dims, L);
+    if (workspace_bytes < L.total) return MOE_SHUFFLE_E_WORKSPACE;
+
+    moe_shuffle_plan_s* p = (moe_shuffle_plan_s*)calloc(1, sizeof(moe_shuffle_plan_s));
+    if (!p) return MOE_SHUFFLE_E_INVALID_ARG;
+    p->dims = *dims;
+    p->L = L;
+    p->ws = (char*)workspace;
+    p->n_known = -1;
+
+    ms::PlanPtrs P;
+    P.idx = topk_idx;
+    P.status = at<int32_t>(p, L.status);
+    P.n_rank_rows = at<int32_t>(p, L.n_rank_rows);
+    P.expert_count = at<int32_t>(p, L.expert_count);
+    P.expert_offset = at<int32_t>(p, L.expert_offset);
+    P.rank_count = at<int32_t>(p, L.rank_count);
+    P.rank_offset = at<int32_t>(p, L.rank_offset);
+    P.send_token = at<int32_t>(p, L.send_token);
+    P.tok_rank_row = at<int32_t>(p, L.tok_rank_row);
+    P.fan_src = at<int32_t>(p, L.fan_src);
+    P.fan_dst = at<int32_t>(p, L.fan_dst);
+    P.comb_row = at<int32_t>(p, L.comb_row);
+    P.rank_segs = at<int32_t>(p, L.rank_segs);
+    P.expert_segs = at<int32_t>(p, L.expert_segs);
+    P.tile_hist = at<int32_t>(p, L.tile_hist);
+    P.tile_base = at<int32_t>(p, L.tile_base);
+    P.col_total = at<int32_t>(p, L.col_total);
+    const hipError_t e = ms::launch_plan(L, P, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        free(p);
+        return hip_fail(e);
+    }
+    *plan = p;
+    return MOE_SHUFFLE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_send(const moe_shuffle_plan_s* plan, const void* x, const void* xr, int64_t xr_rows)
+{
+    const ms::Layout& L = plan->L;
+    if (!x || !xr) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (misaligned(x, 16) || misaligned(xr, 16)) return MOE_SHUFFLE_E_ALIGN;
+    if (xr_rows < rank_rows_needed(plan)) return MOE_SHUFFLE_E_INVALID_ARG;
+    const size_t row = (size_t)L.H * 2;
+    if (overlap(x, row * L.T, xr, row * (size_t)xr_rows)) return MOE_SHUFFLE_E_INVALID_ARG;
+    return MOE_SHUFFLE_OK;
+}
+
+int check_fanout(const moe_shuffle_plan_s* plan, const void* xr, int64_t xr_rows, const void* xe)
+{
+    const ms::Layout& L = plan->L;
+    if (!xr || !xe) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (misaligned(xe, 16) || misaligned(xr, 16)) return MOE_SHUFFLE_E_ALIGN;
+    if (xr_rows < rank_rows_needed(plan)) return MOE_SHUFFLE_E_INVALID_ARG;
+    const size_t row = (size_t)L.H * 2;
+    if (overlap(xe, row * (size_t)L.T * L.k, xr, row * (size_t)xr_rows)) return MOE_SHUFFLE_E_INVALID_ARG;
+    return MOE_SHUFFLE_OK;
+}
+
+hipError_t launch_send(const moe_shuffle_plan_s* plan, const void* x, void* xr, void* stream)
+{
+    const ms::Layout& L = plan->L;
+    return ms::launch_fanout_rows(x, xr, at<int32_t>(plan, L.tok_rank_row), L.KR, L.T, nullptr, L.H,
+                                  at<int32_t>(plan, L.status), (hipStream_t)stream);
+}
+
+hipError_t launch_fanout(const moe_shuffle_plan_s* plan, const void* xr, void* xe, void* stream)
+{
+    const ms::Layout& L = plan->L;
+    return ms::launch_fanout_rows(xr, xe, at<int32_t>(plan, L.fan_dst), L.D, rank_rows_needed(plan),
+                                  at<int32_t>(plan, L.n_rank_rows), L.H, at<int32_t>(plan, L.status),
+                                  (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_shuffle_dispatch_send(moe_shuffle_plan_t plan, const void* x, void* xr, int64_t xr_rows, void* stream)
+{
+    int rc = check_plan(plan);
+    if (rc) return rc;
+    if (plan->L.T == 0) return MOE_SHUFFLE_OK;
+    rc = check_send(plan, x, xr, xr_rows);
+    if (rc) return rc;
+    const hipError_t e = launch_send(plan, x, xr, stream);
+    return e == hipSuccess ? MOE_SHUFFLE_OK : hip_fail(e);
+}
+
+int moe_shuffle_dispatch_fanout(moe_shuffle_plan_t plan, const void* xr, int64_t xr_rows, void* xe, void* stream)
+{
+    int rc = check_plan(plan);
+    if (rc) return rc;
+    if (plan->L.T == 0) return MOE_SHUFFLE_OK;
+    rc = check_fanout(plan, xr, xr_rows, xe);
+    if (rc) return rc;
+    const hipError_t e = launch_fanout(plan, xr, xe, stream);
+    return e == hipSuccess ? MOE_SHUFFLE_OK : hip_fail(e);
+}
+
+int moe_shuffle_dispatch(moe_shuffle_plan_t plan, const void* x, void* xr, int64_t xr_rows, void* xe, void* stream)
+{
+    int rc = check_plan(plan);
+    if (rc) return rc;
+    const ms::Layout& L = plan->L;
+    if (L.T == 0) return MOE_SHUFFLE_OK;
+    // every check before the first launch, so a failing call writes nothing
+    rc = check_send(plan, x, xr, xr_rows);
+    if (rc) return rc;
+    rc = check_fanout(plan, xr, xr_rows, xe);
+    if (rc) return rc;
+    const size_t row = (size_t)L.H * 2;
+    if (overlap(x, row * L.T, xe, row * (size_t)L.T * L.k)) return MOE_SHUFFLE_E_INVALID_ARG;
+    hipError_t e = launch_send(plan, x, xr, stream);
+    if (e == hipSuccess) e = launch_fanout(plan, xr, xe, stream);
+    return e == hipSuccess ? MOE_SHUFFLE_OK : hip_fail(e);
+}
+
+int moe_shuffle_combine(moe_shuffle_plan_t plan, const void* ye, const float* topk_w, void* out, void* stream)
+{
+    int rc = check_plan(plan);
+    if (rc) return rc;
+    const ms::Layout& L = plan->L;
+    if (L.T == 0) return MOE_SHUFFLE_OK;
+    if (!ye || !topk_w || !out) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (misaligned(ye, 16) || misaligned(out, 16) || misaligned(topk_w, 4)) return MOE_SHUFFLE_E_ALIGN;
+    const size_t row = (size_t)L.H * 2;
+    if (overlap(ye, row * (size_t)L.T * L.k, out, row * L.T)) return MOE_SHUFFLE_E_INVALID_ARG;
+    const hipError_t e = ms::launch_combine_rows(ye, topk_w, at<int32_t>(plan, L.comb_row), out, L.T, L.k, L.H,
+                                                 at<int32_t>(plan, L.status), (hipStream_t)stream);
+    return e == hipSuccess ? MOE_SHUFFLE_OK : hip_fail(e);
+}
+
+int moe_shuffle_plan_query(moe_shuffle_plan_t plan, void* stream, moe_shuffle_plan_info* info)
+{
+    int rc = check_plan(plan);
+    if (rc) return rc;
+    if (!info) return MOE_SHUFFLE_E_INVALID_ARG;
+    int32_t st = 0, n = 0;
+    hipError_t e = hipMemcpyAsync(&st, at<int32_t>(plan, plan->L.status), sizeof st, hipMemcpyDeviceToHost,
+                                  (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(&n, at<int32_t>(plan, plan->L.n_rank_rows), sizeof n, hipMemcpyDeviceToHost,
+                           (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    info->status = st;
+    info->n_rank_rows = st == MOE_SHUFFLE_OK ? n : 0;
+    info->n_expert_rows = plan->L.T * plan->L.k;
+    info->max_rank_rows = plan->L.T * plan->L.KR;
+    if (st == MOE_SHUFFLE_OK) plan->n_known = n;
+    return st;
+}
+
+int moe_shuffle_plan_arrays_get(moe_shuffle_plan_t plan, moe_shuffle_plan_arrays* a)
+{
+    int rc = check_plan(plan);
+    if (rc) return rc;
+    if (!a) return MOE_SHUFFLE_E_INVALID_ARG;
+    const ms::Layout& L = plan->L;
+    a->expert_count = at<int32_t>(plan, L.expert_count);
+    a->expert_offset = at<int32_t>(plan, L.expert_offset);
+    a->rank_count = at<int32_t>(plan, L.rank_count);
+    a->rank_offset = at<int32_t>(plan, L.rank_offset);
+    a->send_token = at<int32_t>(plan, L.send_token);
+    a->tok_rank_row = at<int32_t>(plan, L.tok_rank_row);
+    a->fan_src = at<int32_t>(plan, L.fan_src);
+    a->fan_dst = at<int32_t>(plan, L.fan_dst);
+    a->comb_row = at<int32_t>(plan, L.comb_row);
+    a->rank_segs = at<moe_segment>(plan, L.rank_segs);
+    a->expert_segs = at<moe_segment>(plan, L.expert_segs);
+    a->status = at<int32_t>(plan, L.status);
+    a->n_rank_rows = at<int32_t>(plan, L.n_rank_rows);
+    a->tok_rank_width = L.KR;
+    a->fan_dst_width = L.D;
+    return MOE_SHUFFLE_OK;
+}
+
+void moe_shuffle_plan_destroy(moe_shuffle_plan_t plan) { free(plan); }
+
+const char* moe_shuffle_strerror(int code)
+{
+    switch (code) {
+        case MOE_SHUFFLE_OK: return "ok";
+        case MOE_SHUFFLE_E_INVALID_ARG: return "invalid argument";
+        case MOE_SHUFFLE_E_ALIGN: return "misaligned size or pointer";
+        case MOE_SHUFFLE_E_WORKSPACE: return "workspace too small";
+        case MOE_SHUFFLE_E_BAD_INDEX: return "top-k id out of range or repeated within a token";
+        case MOE_SHUFFLE_E_HIP: return "HIP runtime error";
+        case MOE_SHUFFLE_E_OVERFLOW: return "size beyond implementation limits";
+        default: return "unknown status";
+    }
+}
+
+int moe_shuffle_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// internal.h -- workspace layout and kernel launchers shared by abi.hip and
+// shuffle_kernels.hip (library-internal; not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_shuffle.h"
+
+namespace ms {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kBlock = 256;        // threads per block for every kernel
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kPlanTile = kBlock;  // tokens per plan block (one per thread)
+constexpr int kMaxTopK = 64;
+constexpr int kMaxCols = 1024;     // E + R: histogram columns per token tile
+
+// Byte offsets of every array inside the caller's workspace.  Each array
+// starts on a 256-byte boundary.
+struct Layout {
+    int T, H, E, k, R, Epr, KR, D, C, ntiles;
+    size_t status, n_rank_rows;
+    size_t expert_count, expert_offset, rank_count, rank_offset;
+    size_t send_token, tok_rank_row, fan_src, fan_dst, comb_row;
+    size_t rank_segs, expert_segs;
+    size_t tile_hist, tile_base, col_total;
+    size_t total;
+};
+
+// Fills `L` from validated dims.
+void make_layout(const moe_shuffle_dims& d, Layout& L);
+
+struct PlanPtrs {
+    const int32_t* idx;
+    int32_t *status, *n_rank_rows;
+    int32_t *expert_count, *expert_offset, *rank_count, *rank_offset;
+    int32_t *send_token, *tok_rank_row, *fan_src, *fan_dst, *comb_row;
+    int32_t *rank_segs, *expert_segs;
+    int32_t *tile_hist, *tile_base, *col_total;
+};
+
+// Each launcher returns the hipError_t of its launch(es).
+hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s);
+
+// dst[map[u][d]] = src[u] for every source row u < n and every map entry
+// d < width that is not -1.  n is read from n_dev when it is non-null (then
+// n_bound bounds it); otherwise n = n_bound.
+hipError_t launch_fanout_rows(const void* src, void* dst, const int32_t* map, int width,
+                              int64_t n_bound, const int32_t* n_dev, int H,
+                              const int32_t* status, hipStream_t s);
+
+// out[t] = bf16( fp32 fma chain over j of w[t][j] * ye[rows[t][j]] ).
+hipError_t launch_combine_rows(const void* ye, const float* w, const int32_t* rows, void* out,
+                               int T, int k, int H, const int32_t* status, hipStream_t s);
+
+}  // namespace ms

@@ -30,7 +30,8 @@ import dataclasses
 import numpy as np
 
 __all__ = ["Config", "CONFIGS", "make_x", "make_routing", "make_inputs",
-           "random_routing", "random_bf16", "f32_to_bf16_bits", "bf16_bits_to_f32"]
+           "random_routing", "random_bf16", "f32_to_bf16_bits", "bf16_bits_to_f32", "make_expert_outputs",
+           "wide_bf16"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -146,3 +147,23 @@ def random_routing(rng: np.random.Generator, T: int, E: int, k: int, signed_gate
 
 def random_bf16(rng: np.random.Generator, shape, scale: float = 1.0) -> np.ndarray:
     return f32_to_bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+def wide_bf16(rng: np.random.Generator, shape, emin: int = -15, emax: int = 15) -> np.ndarray:
+    """Random finite bf16 bit patterns: random sign and mantissa, exponent
+    uniform in [emin, emax] (so sums cancel and round in many binades)."""
+    r = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    e = rng.integers(127 + emin, 127 + emax + 1, size=shape, dtype=np.uint16)
+    return ((r & np.uint16(0x807F)) | (e << np.uint16(7))).astype(np.uint16)
+
+
+def make_expert_outputs(cfg: Config, seed: int = 0, chunk_rows: int = 16384) -> np.ndarray:
+    """Stand-in expert outputs ye[T*k, H] (bf16 bits) for combine tests: the
+    pages' experts are dense FFNs with trained weights, which are not here."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(3)[2]))
+    rows = cfg.T * cfg.k
+    out = np.empty((rows, cfg.H), dtype=np.uint16)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        out[r0:r1] = wide_bf16(rng, (r1 - r0, cfg.H))
+    return out

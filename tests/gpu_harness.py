@@ -1,0 +1,102 @@
+"""Runs the HIP path through the C ABI on seeded inputs and the oracle on the
+same inputs, and compares them (GPU tests only)."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import moe_expert_token_amd as ms
+import oracle
+import pins
+
+SENTINEL = 0x7FC1  # a NaN pattern no kernel ever writes: marks rows left untouched
+
+PLAN_KEYS = ("expert_count", "expert_offset", "rank_count", "rank_offset", "send_token", "tok_rank_row",
+             "fan_src", "fan_dst", "comb_row", "rank_segs", "expert_segs")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+def to_host16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def run_hip(idx: np.ndarray, x: np.ndarray, w: np.ndarray, H: int, E: int, R: int, ye: np.ndarray | None = None,
+            query_first: bool = True):
+    """plan -> (query) -> dispatch -> combine(ye or xe).  Returns host copies."""
+    T, k = idx.shape
+    dims = ms.dims_of(T, H, E, k, R)
+    ws = torch.empty(ms.moe_shuffle_workspace_size(dims), dtype=torch.uint8, device="cuda")
+    idx_d = torch.from_numpy(np.ascontiguousarray(idx)).cuda()
+    plan = ms.moe_shuffle_plan(dims, idx_d, ws)
+    info = ms.moe_shuffle_plan_query(plan) if query_first else None
+    KR = min(k, R)
+    xr = torch.full((max(T * KR, 1), H), SENTINEL, dtype=torch.int16, device="cuda")
+    xe = torch.full((max(T * k, 1), H), SENTINEL, dtype=torch.int16, device="cuda")
+    x_d = to_dev16(x) if T else torch.empty((1, H), dtype=torch.int16, device="cuda")
+    ms.moe_shuffle_dispatch(plan, x_d, xr, xe)
+    w_d = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).cuda() if T else \
+        torch.empty(1, dtype=torch.float32, device="cuda")
+    out = torch.full((max(T, 1), H), SENTINEL, dtype=torch.int16, device="cuda")
+    out_rt = torch.full((max(T, 1), H), SENTINEL, dtype=torch.int16, device="cuda")
+    ms.moe_shuffle_combine(plan, xe, w_d, out_rt)          # identity expert: ye is xe itself
+    if ye is not None:
+        ms.moe_shuffle_combine(plan, to_dev16(ye), w_d, out)
+    if info is None:
+        info = ms.moe_shuffle_plan_query(plan)
+    torch.cuda.synchronize()
+    N = info["N"]
+    v = ms.plan_array_views(plan, N)
+    res = {key: v[key].cpu().numpy() for key in PLAN_KEYS}
+    res["N"] = N
+    res["status"] = info["status"]
+    res["xr"] = to_host16(xr)
+    res["xe"] = to_host16(xe)[:T * k]
+    res["out_rt"] = to_host16(out_rt)[:T]
+    res["out"] = to_host16(out)[:T] if ye is not None else res["out_rt"]
+    ms.moe_shuffle_plan_destroy(plan)
+    return res
+
+
+def compare_plan(g: dict, o: dict):
+    assert g["N"] == o["N"], (g["N"], o["N"])
+    for key in PLAN_KEYS:
+        np.testing.assert_array_equal(g[key], o[key], err_msg=f"plan array {key}")
+
+
+def check_case(idx, x, w, H, E, R, ye=None, name=""):
+    """Full parity of one case: plan and dispatch bit-exact, combine <= 1 ulp
+    (0 expected), rank rows past N untouched."""
+    T, k = idx.shape
+    orc = oracle.get()
+    say(f"[case] {name} T={T} H={H} E={E} k={k} R={R}")
+    g = run_hip(idx, x, w, H, E, R, ye)
+    assert g["status"] == 0
+    rc, o = orc.plan(idx, H, E, R)
+    assert rc == 0
+    compare_plan(g, o)
+    N = o["N"]
+    oxr, oxe = orc.dispatch(o, x, E, k, R)
+    np.testing.assert_array_equal(g["xr"][:N], oxr, err_msg="xr")
+    assert np.all(g["xr"][N:] == SENTINEL), "rows past N were written"
+    np.testing.assert_array_equal(g["xe"], oxe, err_msg="xe")
+    oout = orc.combine(o["comb_row"], oxe if ye is None else ye, w, E, R)
+    d = pins.bf16_ulp_distance(g["out"], oout)
+    maxd = int(d.max()) if d.size else 0
+    say(f"[case] {name} N={N} combine max ulp {maxd}, differing {int((d > 0).sum())}")
+    assert maxd <= 1
+    if ye is not None:
+        ort = orc.combine(o["comb_row"], oxe, w, E, R)
+        drt = pins.bf16_ulp_distance(g["out_rt"], ort)
+        assert (int(drt.max()) if drt.size else 0) <= 1
+    return g, o

@@ -1,0 +1,89 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and its host-side checks agree with the oracle's (no GPU calls)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    import moe_expert_token_amd as ms
+    return ms, ms.load()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "moe_shuffle.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_shuffle_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    ms, lib = _lib()
+    names = header_functions()
+    assert len(names) == 11, names
+    assert sorted(ms.EXPORTS) == names
+    for n in names:
+        assert getattr(lib, n) is not None
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+DIMS = [(4, 8, 8, 2, 4), (0, 8, 8, 2, 4), (-1, 8, 8, 2, 4), (4, 0, 8, 2, 4), (4, 8, 0, 2, 4), (4, 8, 8, 0, 4),
+        (4, 8, 8, 2, 0), (4, 8, 8, 9, 4), (4, 8, 8, 2, 3), (4, 12, 8, 2, 4), (1 << 28, 8, 16, 8, 4),
+        (8192, 7168, 256, 8, 32), (65536, 4096, 128, 8, 16)]
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_dims_codes_match_oracle(d):
+    ms, lib = _lib()
+    want = oracle.get().check_dims(*d)
+    try:
+        ms.moe_shuffle_workspace_size(ms.dims_of(*d))
+        got = 0
+    except ms.MoeShuffleError as e:
+        got = e.code
+    assert got == want
+
+
+def test_implementation_limits():
+    ms, lib = _lib()
+    for d in [(4, 8, 128, 65, 4), (4, 8, 1024, 2, 8)]:
+        with pytest.raises(ms.MoeShuffleError) as e:
+            ms.moe_shuffle_workspace_size(ms.dims_of(*d))
+        assert e.value.code == ms.E_OVERFLOW
+    assert ms.moe_shuffle_workspace_size(ms.dims_of(4, 8, 1024 - 64, 8, 64)) > 0
+
+
+def test_plan_rejects_bad_pointers_before_any_launch():
+    ms, lib = _lib()
+    d = ms.dims_of(4, 8, 8, 2, 4)
+    h = ctypes.c_void_p(0)
+    n = ms.moe_shuffle_workspace_size(d)
+    # null workspace, misaligned workspace, too small workspace: rejected on the host
+    assert lib.moe_shuffle_plan(ctypes.byref(d), 0x1000, None, n, None, ctypes.byref(h)) == ms.E_INVALID_ARG
+    assert lib.moe_shuffle_plan(ctypes.byref(d), 0x1000, 0x10010, n, None, ctypes.byref(h)) == ms.E_ALIGN
+    assert lib.moe_shuffle_plan(ctypes.byref(d), 0x1000, 0x10000, n - 1, None, ctypes.byref(h)) == ms.E_WORKSPACE
+    assert lib.moe_shuffle_plan(ctypes.byref(d), None, 0x10000, n, None, ctypes.byref(h)) == ms.E_INVALID_ARG
+
+
+def test_strerror_and_null_handles():
+    ms, lib = _lib()
+    for c in (0, -1, -2, -3, -4, -5, -6):
+        assert ms.moe_shuffle_strerror(c)
+    assert lib.moe_shuffle_dispatch(None, None, None, 0, None, None) == ms.E_INVALID_ARG
+    assert lib.moe_shuffle_combine(None, None, None, None, None) == ms.E_INVALID_ARG
+    lib.moe_shuffle_plan_destroy(None)
+
+
+def test_product_package_does_not_reach_the_oracle():
+    pkg = os.path.join(ROOT, "moe_expert_token_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f

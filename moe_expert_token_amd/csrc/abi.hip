@@ -185,14 +185,14 @@ int check_fanout(const moe_shuffle_plan_s* plan, const void* xr, int64_t xr_rows
 hipError_t launch_send(const moe_shuffle_plan_s* plan, const void* x, void* xr, void* stream)
 {
     const ms::Layout& L = plan->L;
-    return ms::launch_fanout_rows(x, xr, at<int32_t>(plan, L.tok_rank_row), L.KR, L.T, nullptr, L.H,
+    return ms::launch_fanout_rows(true, x, xr, at<int32_t>(plan, L.tok_rank_row), L.KR, L.T, nullptr, L.H,
                                   at<int32_t>(plan, L.status), (hipStream_t)stream);
 }
 
 hipError_t launch_fanout(const moe_shuffle_plan_s* plan, const void* xr, void* xe, void* stream)
 {
     const ms::Layout& L = plan->L;
-    return ms::launch_fanout_rows(xr, xe, at<int32_t>(plan, L.fan_dst), L.D, rank_rows_needed(plan),
+    return ms::launch_fanout_rows(false, xr, xe, at<int32_t>(plan, L.fan_dst), L.D, rank_rows_needed(plan),
                                   at<int32_t>(plan, L.n_rank_rows), L.H, at<int32_t>(plan, L.status),
                                   (hipStream_t)stream);
 }

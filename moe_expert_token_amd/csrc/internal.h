@@ -46,8 +46,9 @@ hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s);
 
 // dst[map[u][d]] = src[u] for every source row u < n and every map entry
 // d < width that is not -1.  n is read from n_dev when it is non-null (then
-// n_bound bounds it); otherwise n = n_bound.
-hipError_t launch_fanout_rows(const void* src, void* dst, const int32_t* map, int width,
+// n_bound bounds it); otherwise n = n_bound.  `send` picks the kernel name
+// (send: x -> xr; otherwise fan-out: xr -> xe).
+hipError_t launch_fanout_rows(bool send, const void* src, void* dst, const int32_t* map, int width,
                               int64_t n_bound, const int32_t* n_dev, int H,
                               const int32_t* status, hipStream_t s);
 

@@ -54,10 +54,14 @@ def source_digest() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(workload: str, kernel: str, per_launch_alg: float):
+KERNEL_NAMES = {"plan": "plan_count/scan/place", "send": "dispatch_send_kernel",
+                "fanout": "dispatch_fanout_kernel", "combine": "combine_rows_kernel"}
+
+
+def load_traffic(workload: str, kernel: str):
     """HBM traffic from the committed rocprofv3 counter summary, only while the
     kernel source still matches the one that was profiled."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{KERNEL_NAMES[kernel]}_{workload}.json")
     if not os.path.exists(path):
         return None
     try:
@@ -67,6 +71,88 @@ def load_traffic(workload: str, kernel: str, per_launch_alg: float):
     if rec.get("kernel_src_sha256_16") != source_digest():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def n_rank_rows(topk_idx, E, R):
+    """Distinct (token, rank) pairs of a routing (bookkeeping for byte counts)."""
+    import numpy as np
+    T = topk_idx.shape[0]
+    pairs = np.arange(T, dtype=np.int64)[:, None] * R + topk_idx // (E // R)
+    return int(np.unique(pairs).size)
+
+
+def pmc_summary(args):
+    """Turns two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and one kernel
+    trace of this bench into profiles/: a markdown table per workload and one
+    traffic record per kernel.  FETCH_SIZE / WRITE_SIZE are KiB per dispatch;
+    each is scaled by what it reads for the runtime's copy kernel of known
+    size in the same run (the bench's copy-ceiling leg)."""
+    import csv
+    import collections
+
+    import synth
+    cfg = synth.CONFIGS[args.config]
+    T, H, E, k, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.R
+    idx, _ = synth.make_routing(cfg, args.seed)
+    N = n_rank_rows(idx, E, R)
+    B = algorithmic_bytes(T, H, k, N)
+    copy_bytes = min(T * k * H * 2, 2 << 30)
+
+    def per_kernel(path):
+        vals = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(args.fetch_csv), per_kernel(args.write_csv)
+    copy_name = next(n for n in fetch if "copyBuffer" in n)
+    f_factor = copy_bytes / (max(fetch[copy_name]) * 1024)
+    w_factor = copy_bytes / (max(write[copy_name]) * 1024)
+    stats = {r["Name"]: r for r in csv.DictReader(open(args.trace_stats))}
+
+    short = {"dispatch_send_kernel": "send", "dispatch_fanout_kernel": "fanout", "combine_rows_kernel": "combine"}
+    digest = source_digest()
+    rows = []
+    for name in sorted(set(fetch) & set(write)):
+        if "copyBuffer" in name:
+            continue
+        base = name.split("(")[0].replace("void ", "").split("<")[0].replace("ms::", "")
+        fb = sum(fetch[name]) / len(fetch[name]) * 1024 * f_factor
+        wb = sum(write[name]) / len(write[name]) * 1024 * w_factor
+        st = next((r for n, r in stats.items() if n.split("(")[0] == name.split("(")[0]), None)
+        avg_us = float(st["AverageNs"]) / 1e3 if st else float("nan")
+        alg = B.get(short.get(base, ""), None)
+        rows.append((base, name.split("(")[0], avg_us, fb, wb, alg))
+        if alg is not None:
+            rec = {"kernel": base, "workload": cfg.name, "kernel_src_sha256_16": digest,
+                   "hbm_bytes_per_launch": round(fb + wb), "fetch_bytes_per_launch": round(fb),
+                   "write_bytes_per_launch": round(wb), "alg_bytes_per_launch": alg,
+                   "traffic_over_alg": round((fb + wb) / alg, 4),
+                   "fetch_scale": round(f_factor, 4), "write_scale": round(w_factor, 4),
+                   "copy_kernel_bytes": copy_bytes, "commands": args.commands}
+            with open(os.path.join(args.out_dir, f"traffic_{base}_{cfg.name}.json"), "w") as f:
+                json.dump(rec, f, indent=1)
+    lines = [f"# Kernel time and HBM traffic — {cfg.name}", "",
+             f"T={T} H={H} E={E} k={k} R={R}, N={N} deduplicated rank rows; kernel source sha256[:16] {digest}.", "",
+             "Commands (run from the repository root on one MI355X):", ""]
+    lines += [f"    {c}" for c in args.commands] + [""]
+    lines += [f"Counter scale from the runtime copy kernel of {copy_bytes} bytes in the same runs: "
+              f"FETCH_SIZE x {f_factor:.4f}, WRITE_SIZE x {w_factor:.4f}.", "",
+              "| kernel | avg us (trace) | HBM read MB | HBM write MB | algorithmic MB | traffic / alg | GB/s alg |",
+              "|---|---|---|---|---|---|---|"]
+    for base, full, us, fb, wb, alg in sorted(rows, key=lambda r: -r[2] if r[2] == r[2] else 0):
+        ratio = f"{(fb + wb) / alg:.3f}" if alg else "-"
+        gbs = f"{alg / (us * 1e-6) / 1e9:.0f}" if alg and us == us else "-"
+        lines.append(f"| `{full}` | {us:.1f} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
+                     f"{(alg / 1e6 if alg else float('nan')):.1f} | {ratio} | {gbs} |")
+    lines += ["", "Kernel trace summary (rocprofv3 --stats):", "", "| kernel | calls | avg us | min us | max us |",
+              "|---|---|---|---|---|"]
+    for n, r in stats.items():
+        lines.append(f"| `{n.split('(')[0]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    with open(os.path.join(args.out_dir, f"kernels_{cfg.name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def main():
@@ -79,7 +165,16 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=12.0, help="CPU-oracle timing budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--pmc-summary", action="store_true", help="summarise rocprofv3 CSVs into profiles/ (no GPU)")
+    ap.add_argument("--fetch-csv")
+    ap.add_argument("--write-csv")
+    ap.add_argument("--trace-stats")
+    ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--commands", nargs="*", default=[])
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -107,7 +202,13 @@ def main():
     KR = min(k, R)
     log(f"[bench] workload {cfg.name}: generating inputs")
     inp = synth.make_inputs(cfg, args.seed)
-    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev)
+    # Each step takes the next of NB resident copies of the batch, NB * |x| >=
+    # 512 MiB (twice the 256 MiB memory-side cache), so no step finds the
+    # previous step's activations still cached.
+    x_bytes = T * H * 2
+    nb = int(min(8, max(2, -(-(512 << 20) // max(x_bytes, 1)))))
+    x0 = torch.from_numpy(inp["x"].view(np.int16)).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(nb - 1)]
     idx = torch.from_numpy(inp["topk_idx"]).to(dev)
     w = torch.from_numpy(inp["topk_w"]).to(dev)
     dims = ms.dims_of(T, H, E, k, R)
@@ -117,7 +218,11 @@ def main():
     out = torch.empty((T, H), dtype=torch.int16, device=dev)
     torch.cuda.synchronize()
 
+    counter = [0]
+
     def step(ev=None):
+        x = xs[counter[0] % nb]
+        counter[0] += 1
         if ev is not None:
             ev[0].record()
         plan = ms.moe_shuffle_plan(dims, idx, ws)
@@ -216,7 +321,7 @@ def main():
     # dominant kernel by algorithmic bytes: the receiver fan-out
     dom = max(("send", "fanout", "combine"), key=lambda n: B[n])
     achieved = B[dom] / (us[dom] * 1e-6) / 1e9
-    traffic = load_traffic(cfg.name, dom, B[dom])
+    traffic = load_traffic(cfg.name, dom)
     dc_us = us["send"] + us["fanout"] + us["combine"]
     value = B["total"] / (ms_per_step * 1e-3) / 1e9
     rec = {
@@ -224,7 +329,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "H": H, "E": E, "k": k, "R": R, "N": N,
-                   "parallelism": f"ep{R}-logical-on-1gpu"},
+                   "parallelism": f"ep{R}-logical-on-1gpu", "rotating_batches": nb},
         "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "dispatch_combine_GBps": round((B["send"] + B["fanout"] + B["combine"]) / (dc_us * 1e-6) / 1e9, 1),
@@ -233,7 +338,7 @@ def main():
         "algorithmic_bytes": B,
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "accumulate": "fp32",
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+        "roofline": {"kernel": KERNEL_NAMES[dom], "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": B[dom], "avg_launch_us": round(us[dom], 2)},
         "cpu_baseline": cpu,

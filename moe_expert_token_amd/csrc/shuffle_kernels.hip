@@ -378,6 +378,47 @@ hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)
 // LDS with one coalesced load; each wave then broadcasts its targets as
 // scalars.
 
+// 16-byte row traffic, with or without the non-temporal hint.  Which side of
+// which kernel carries the hint was chosen by measurement on the MI355X (the
+// hint changes how lines are kept in L2 and the memory-side cache):
+//   send     plain loads, plain stores (its scattered row writes go through L2)
+//   fan-out  non-temporal loads and stores
+//   combine  non-temporal loads and stores
+// (DeepSeek-V3-like workload: send 153 us with plain stores against 178 us
+// with non-temporal ones; fan-out 303 us against 324 us with plain loads.)
+#ifndef MS_SEND_NT_LOAD
+#define MS_SEND_NT_LOAD 0
+#endif
+#ifndef MS_SEND_NT_STORE
+#define MS_SEND_NT_STORE 0
+#endif
+#ifndef MS_FANOUT_NT_LOAD
+#define MS_FANOUT_NT_LOAD 1
+#endif
+#ifndef MS_FANOUT_NT_STORE
+#define MS_FANOUT_NT_STORE 1
+#endif
+#ifndef MS_COMBINE_NT_LOAD
+#define MS_COMBINE_NT_LOAD 1
+#endif
+#ifndef MS_COMBINE_NT_STORE
+#define MS_COMBINE_NT_STORE 1
+#endif
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load_row16(const u32x4* p)
+{
+    if (NT) return __builtin_nontemporal_load(p);
+    return *p;
+}
+
+template <bool NT>
+__device__ __forceinline__ void store_row16(u32x4 v, u32x4* p)
+{
+    if (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
 struct RowSplit {
     int V;        // 16-byte vectors per row
     int cpr;      // chunks per row
@@ -397,7 +438,7 @@ __device__ __forceinline__ void block_rows(int64_t n, const RowSplit& rs, int* f
 
 // Body shared by the send and fan-out kernels (two names, so that traces and
 // counters tell the two halves of dispatch apart).
-template <int U, bool FULL>
+template <int U, bool FULL, bool NTL, bool NTS>
 __device__ __forceinline__ void fanout_rows(int* s_tile, const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                             const int32_t* __restrict__ map, int width, int64_t n_bound,
                                             const int32_t* __restrict__ n_dev, RowSplit rs,
@@ -421,7 +462,7 @@ __device__ __forceinline__ void fanout_rows(int* s_tile, const u32x4* __restrict
     u32x4 v[U];
 #pragma unroll
     for (int i = 0; i < U; ++i)
-        if (FULL || c0 + i * kWave + lane < V) v[i] = __builtin_nontemporal_load(s + i * kWave + lane);
+        if (FULL || c0 + i * kWave + lane < V) v[i] = load_row16<NTL>(s + i * kWave + lane);
     const int* targets = s_tile + (row - first) * width;
     for (int d = 0; d < width; ++d) {
         const int p = __builtin_amdgcn_readfirstlane(targets[d]);
@@ -429,11 +470,11 @@ __device__ __forceinline__ void fanout_rows(int* s_tile, const u32x4* __restrict
         u32x4* o = dst + (int64_t)p * V + c0;
 #pragma unroll
         for (int i = 0; i < U; ++i)
-            if (FULL || c0 + i * kWave + lane < V) __builtin_nontemporal_store(v[i], o + i * kWave + lane);
+            if (FULL || c0 + i * kWave + lane < V) store_row16<NTS>(v[i], o + i * kWave + lane);
     }
 }
 
-#define MS_FANOUT_KERNEL(NAME)                                                                                  \
+#define MS_FANOUT_KERNEL(NAME, NTL, NTS)                                                                        \
     template <int U, bool FULL>                                                                                  \
     __global__ __launch_bounds__(kBlock) void NAME(const u32x4* __restrict__ src, u32x4* __restrict__ dst,       \
                                                    const int32_t* __restrict__ map, int width, int64_t n_bound,  \
@@ -441,22 +482,30 @@ __device__ __forceinline__ void fanout_rows(int* s_tile, const u32x4* __restrict
                                                    const int32_t* __restrict__ status)                          \
     {                                                                                                            \
         extern __shared__ int s_tile[]; /* [rows of this block][width] */                                        \
-        fanout_rows<U, FULL>(s_tile, src, dst, map, width, n_bound, n_dev, rs, status);                          \
+        fanout_rows<U, FULL, NTL, NTS>(s_tile, src, dst, map, width, n_bound, n_dev, rs, status);                \
     }
 // x -> xr: source rows are tokens, targets their rank rows.
-MS_FANOUT_KERNEL(dispatch_send_kernel)
+MS_FANOUT_KERNEL(dispatch_send_kernel, MS_SEND_NT_LOAD, MS_SEND_NT_STORE)
 // xr -> xe: source rows are rank rows, targets the receiver's expert rows.
-MS_FANOUT_KERNEL(dispatch_fanout_kernel)
+MS_FANOUT_KERNEL(dispatch_fanout_kernel, MS_FANOUT_NT_LOAD, MS_FANOUT_NT_STORE)
 #undef MS_FANOUT_KERNEL
 
-// Vectors per lane of a unit.
-constexpr int kUnitVectors = 1;
+// Vectors per lane of a unit (a unit is 64*U vectors of one row).
+#ifndef MS_SEND_UNIT
+#define MS_SEND_UNIT 1
+#endif
+#ifndef MS_FANOUT_UNIT
+#define MS_FANOUT_UNIT 1
+#endif
+#ifndef MS_COMBINE_UNIT
+#define MS_COMBINE_UNIT 1
+#endif
 
-// Splits rows of V vectors into chunks; false if rows * chunks overflows int.
-static bool make_split(int V, int64_t rows, RowSplit* rs)
+// Splits rows of V vectors into chunks of 64*U; false if rows * chunks overflows int.
+static bool make_split(int V, int U, int64_t rows, RowSplit* rs)
 {
     rs->V = V;
-    rs->cpr = (V + kWave * kUnitVectors - 1) / (kWave * kUnitVectors);
+    rs->cpr = (V + kWave * U - 1) / (kWave * U);
     rs->div = make_fastdiv(rs->cpr);
     return rows * rs->cpr + kWavesPerBlock < ((int64_t)1 << 31);
 }
@@ -466,31 +515,52 @@ static size_t tile_lds_bytes(int width, int arrays)
     return sizeof(int) * (size_t)arrays * kWavesPerBlock * width;  // at most one row per wave
 }
 
-hipError_t launch_fanout_rows(bool send, const void* src, void* dst, const int32_t* map, int width, int64_t n_bound,
-                              const int32_t* n_dev, int H, const int32_t* status, hipStream_t s)
+template <int U>
+static hipError_t launch_fanout_u(bool send, const void* src, void* dst, const int32_t* map, int width,
+                                  int64_t n_bound, const int32_t* n_dev, int V, const int32_t* status, hipStream_t s)
 {
-    if (n_bound <= 0) return hipSuccess;
     RowSplit rs;
-    if (!make_split(H / 8, n_bound, &rs)) return hipErrorInvalidValue;
+    if (!make_split(V, U, n_bound, &rs)) return hipErrorInvalidValue;
     const int64_t units = n_bound * rs.cpr;
     const dim3 grid((unsigned)((units + kWavesPerBlock - 1) / kWavesPerBlock));
     const size_t lds = tile_lds_bytes(width, 1);
     const u32x4* sp = (const u32x4*)src;
     u32x4* dp = (u32x4*)dst;
-    const bool full = rs.V % (kWave * kUnitVectors) == 0;
+    const bool full = V % (kWave * U) == 0;
     if (send && full)
-        hipLaunchKernelGGL((dispatch_send_kernel<kUnitVectors, true>), grid, dim3(kBlock), lds, s, sp, dp, map, width,
-                           n_bound, n_dev, rs, status);
+        hipLaunchKernelGGL((dispatch_send_kernel<U, true>), grid, dim3(kBlock), lds, s, sp, dp, map, width, n_bound,
+                           n_dev, rs, status);
     else if (send)
-        hipLaunchKernelGGL((dispatch_send_kernel<kUnitVectors, false>), grid, dim3(kBlock), lds, s, sp, dp, map,
-                           width, n_bound, n_dev, rs, status);
+        hipLaunchKernelGGL((dispatch_send_kernel<U, false>), grid, dim3(kBlock), lds, s, sp, dp, map, width, n_bound,
+                           n_dev, rs, status);
     else if (full)
-        hipLaunchKernelGGL((dispatch_fanout_kernel<kUnitVectors, true>), grid, dim3(kBlock), lds, s, sp, dp, map,
-                           width, n_bound, n_dev, rs, status);
+        hipLaunchKernelGGL((dispatch_fanout_kernel<U, true>), grid, dim3(kBlock), lds, s, sp, dp, map, width, n_bound,
+                           n_dev, rs, status);
     else
-        hipLaunchKernelGGL((dispatch_fanout_kernel<kUnitVectors, false>), grid, dim3(kBlock), lds, s, sp, dp, map,
-                           width, n_bound, n_dev, rs, status);
+        hipLaunchKernelGGL((dispatch_fanout_kernel<U, false>), grid, dim3(kBlock), lds, s, sp, dp, map, width,
+                           n_bound, n_dev, rs, status);
     return hipGetLastError();
+}
+
+// Largest of {1, 2, 4, 8} not above `want` whose chunk does not exceed the row.
+static int fit_unit(int V, int want)
+{
+    int u = want;
+    while (u > 1 && kWave * u > V) u >>= 1;
+    return u;
+}
+
+hipError_t launch_fanout_rows(bool send, const void* src, void* dst, const int32_t* map, int width, int64_t n_bound,
+                              const int32_t* n_dev, int H, const int32_t* status, hipStream_t s)
+{
+    if (n_bound <= 0) return hipSuccess;
+    const int V = H / 8;
+    switch (fit_unit(V, send ? MS_SEND_UNIT : MS_FANOUT_UNIT)) {
+        case 1: return launch_fanout_u<1>(send, src, dst, map, width, n_bound, n_dev, V, status, s);
+        case 2: return launch_fanout_u<2>(send, src, dst, map, width, n_bound, n_dev, V, status, s);
+        case 4: return launch_fanout_u<4>(send, src, dst, map, width, n_bound, n_dev, V, status, s);
+        default: return launch_fanout_u<8>(send, src, dst, map, width, n_bound, n_dev, V, status, s);
+    }
 }
 
 // ---------------------------------------------------------------- combine
@@ -543,7 +613,7 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(const u32x4* __res
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             if (FULL || c0 + i * kWave + lane < V) {
-                const u32x4 v = __builtin_nontemporal_load(y + i * kWave + lane);
+                const u32x4 v = load_row16<MS_COMBINE_NT_LOAD>(y + i * kWave + lane);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     acc[i][2 * e] = __builtin_fmaf(wj, __uint_as_float(v[e] << 16), acc[i][2 * e]);
@@ -559,29 +629,54 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(const u32x4* __res
             u32x4 pk;
 #pragma unroll
             for (int e = 0; e < 4; ++e) pk[e] = bf16_rne(acc[i][2 * e]) | (bf16_rne(acc[i][2 * e + 1]) << 16);
-            __builtin_nontemporal_store(pk, o + i * kWave + lane);
+            store_row16<MS_COMBINE_NT_STORE>(pk, o + i * kWave + lane);
         }
     }
 }
 
-hipError_t launch_combine_rows(const void* ye, const float* w, const int32_t* rows, void* out, int T, int k, int H,
-                               const int32_t* status, hipStream_t s)
+template <int U>
+static hipError_t launch_combine_u(const void* ye, const float* w, const int32_t* rows, void* out, int T, int k, int V,
+                                   const int32_t* status, hipStream_t s)
 {
-    if (T <= 0) return hipSuccess;
     RowSplit rs;
-    if (!make_split(H / 8, T, &rs)) return hipErrorInvalidValue;
+    if (!make_split(V, U, T, &rs)) return hipErrorInvalidValue;
     const int64_t units = (int64_t)T * rs.cpr;
     const dim3 grid((unsigned)((units + kWavesPerBlock - 1) / kWavesPerBlock));
     const size_t lds = tile_lds_bytes(k, 2);
     const u32x4* yp = (const u32x4*)ye;
     u32x4* op = (u32x4*)out;
-    if (rs.V % (kWave * kUnitVectors) == 0)
-        hipLaunchKernelGGL((combine_rows_kernel<kUnitVectors, true>), grid, dim3(kBlock), lds, s, yp, w, rows, op, T, k,
-                           rs, status);
+    if (V % (kWave * U) == 0)
+        hipLaunchKernelGGL((combine_rows_kernel<U, true>), grid, dim3(kBlock), lds, s, yp, w, rows, op, T, k, rs,
+                           status);
     else
-        hipLaunchKernelGGL((combine_rows_kernel<kUnitVectors, false>), grid, dim3(kBlock), lds, s, yp, w, rows, op, T,
-                           k, rs, status);
+        hipLaunchKernelGGL((combine_rows_kernel<U, false>), grid, dim3(kBlock), lds, s, yp, w, rows, op, T, k, rs,
+                           status);
     return hipGetLastError();
+}
+
+// Combine gathers from the whole expert-major buffer; past a few GiB of it,
+// whole-row units (8 KiB) measured faster than 1 KiB units on the MI355X
+// (65536 tokens x 8 x 8 KiB: 0.80 ms against 0.94 ms), below it 1 KiB units
+// were as fast or faster.
+#ifndef MS_COMBINE_UNIT_LARGE
+#define MS_COMBINE_UNIT_LARGE 8
+#endif
+#ifndef MS_COMBINE_LARGE_BYTES
+#define MS_COMBINE_LARGE_BYTES (2ll << 30)
+#endif
+
+hipError_t launch_combine_rows(const void* ye, const float* w, const int32_t* rows, void* out, int T, int k, int H,
+                               const int32_t* status, hipStream_t s)
+{
+    if (T <= 0) return hipSuccess;
+    const int V = H / 8;
+    const bool large = (int64_t)T * k * H * 2 > (int64_t)MS_COMBINE_LARGE_BYTES;
+    switch (fit_unit(V, large ? MS_COMBINE_UNIT_LARGE : MS_COMBINE_UNIT)) {
+        case 1: return launch_combine_u<1>(ye, w, rows, out, T, k, V, status, s);
+        case 2: return launch_combine_u<2>(ye, w, rows, out, T, k, V, status, s);
+        case 4: return launch_combine_u<4>(ye, w, rows, out, T, k, V, status, s);
+        default: return launch_combine_u<8>(ye, w, rows, out, T, k, V, status, s);
+    }
 }
 
 }  // namespace ms

@@ -56,8 +56,13 @@ class Oracle:
         self.lib.oracle_plan.argtypes = [ctypes.POINTER(_Dims), vp, ctypes.POINTER(_PlanOut)]
         self.lib.oracle_dispatch.argtypes = [ctypes.POINTER(_Dims), vp, vp, ctypes.c_int32, vp, vp, vp]
         self.lib.oracle_combine.argtypes = [ctypes.POINTER(_Dims), vp, vp, vp, vp]
+        self.lib.oracle_dispatch_backward.argtypes = [ctypes.POINTER(_Dims), vp, vp, ctypes.c_int32, vp, vp, vp]
+        self.lib.oracle_combine_backward.argtypes = [ctypes.POINTER(_Dims), vp, vp, vp, vp, vp, vp]
+        self.lib.oracle_combine_rank_partial.argtypes = [ctypes.POINTER(_Dims), vp, vp, vp, ctypes.c_int32, vp, vp,
+                                                         vp, vp]
         for f in (self.lib.oracle_check_dims, self.lib.oracle_plan, self.lib.oracle_dispatch,
-                  self.lib.oracle_combine):
+                  self.lib.oracle_combine, self.lib.oracle_dispatch_backward, self.lib.oracle_combine_backward,
+                  self.lib.oracle_combine_rank_partial):
             f.restype = ctypes.c_int
 
     @staticmethod
@@ -128,6 +133,61 @@ class Oracle:
         if rc:
             raise RuntimeError(f"oracle_combine: {rc}")
         return out
+
+
+    def dispatch_backward(self, plan: dict, grad_xe: np.ndarray, T: int, E: int, k: int, R: int):
+        """Returns (grad_xr [N,H], grad_x [T,H]) as bf16 bits."""
+        grad_xe = np.ascontiguousarray(grad_xe, dtype=np.uint16)
+        H = grad_xe.shape[1]
+        N = plan["N"]
+        d = self.dims(T, H, E, k, R)
+        gxr = np.zeros((N, H), np.uint16)
+        gx = np.zeros((T, H), np.uint16)
+        fd = np.ascontiguousarray(plan["fan_dst"], dtype=np.int32)
+        tr = np.ascontiguousarray(plan["tok_rank_row"], dtype=np.int32)
+        rc = self.lib.oracle_dispatch_backward(ctypes.byref(d), fd.ctypes.data, tr.ctypes.data, N,
+                                               grad_xe.ctypes.data, gxr.ctypes.data, gx.ctypes.data)
+        if rc:
+            raise RuntimeError(f"oracle_dispatch_backward: {rc}")
+        return gxr, gx
+
+    def combine_backward(self, comb_row: np.ndarray, grad_out: np.ndarray, ye: np.ndarray, w: np.ndarray,
+                         E: int, R: int):
+        """Returns (grad_ye [T*k,H] bf16 bits, grad_w [T,k] float64)."""
+        comb_row = np.ascontiguousarray(comb_row, dtype=np.int32)
+        grad_out = np.ascontiguousarray(grad_out, dtype=np.uint16)
+        ye = np.ascontiguousarray(ye, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        T, k = comb_row.shape
+        H = grad_out.shape[1]
+        d = self.dims(T, H, E, k, R)
+        gye = np.zeros((T * k, H), np.uint16)
+        gw = np.zeros((T, k), np.float64)
+        rc = self.lib.oracle_combine_backward(ctypes.byref(d), comb_row.ctypes.data, grad_out.ctypes.data,
+                                              ye.ctypes.data, w.ctypes.data, gye.ctypes.data, gw.ctypes.data)
+        if rc:
+            raise RuntimeError(f"oracle_combine_backward: {rc}")
+        return gye, gw
+
+    def combine_rank_partial(self, plan: dict, ye: np.ndarray, w: np.ndarray, E: int, R: int):
+        """Returns (partial [N,H], out [T,H]) as bf16 bits."""
+        ye = np.ascontiguousarray(ye, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        T, k = w.shape
+        H = ye.shape[1]
+        N = plan["N"]
+        d = self.dims(T, H, E, k, R)
+        part = np.zeros((N, H), np.uint16)
+        out = np.zeros((T, H), np.uint16)
+        fd = np.ascontiguousarray(plan["fan_dst"], dtype=np.int32)
+        tr = np.ascontiguousarray(plan["tok_rank_row"], dtype=np.int32)
+        cr = np.ascontiguousarray(plan["comb_row"], dtype=np.int32)
+        rc = self.lib.oracle_combine_rank_partial(ctypes.byref(d), fd.ctypes.data, tr.ctypes.data, cr.ctypes.data,
+                                                  N, ye.ctypes.data, w.ctypes.data, part.ctypes.data,
+                                                  out.ctypes.data)
+        if rc:
+            raise RuntimeError(f"oracle_combine_rank_partial: {rc}")
+        return part, out
 
 
 _default = None

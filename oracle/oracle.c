@@ -264,3 +264,121 @@ int oracle_combine(const oracle_dims* d, const int32_t* comb_row, const uint16_t
         }
     return OR_OK;
 }
+
+/* --------------------------------------------------------------------------
+ * Training direction and the deduplicated return path.
+ *
+ * The FUSCO abstract reports end-to-end training latency, so the shuffle
+ * runs backwards too.  The DySHARP write-up (section 2 / Fig. 1) notes that
+ * the results two experts on one device produce for a token can be summed
+ * before they travel back; applied on the return path this gives one row per
+ * (token, rank) pair, exactly as dispatch sends one.  Readings (pages
+ * silent): every sum accumulates in fp32 from +0 in the stated order; rows
+ * that travel between ranks are bf16 (the payload format of the forward
+ * direction); each stored row is rounded once to bf16 (nearest, ties even).
+ * -------------------------------------------------------------------------- */
+
+/* Backward of dispatch (the adjoint of the two copies):
+ *   grad_xr[p] = bf16( sum over the expert rows q that rank row p fed, q
+ *                      ascending, of grad_xe[q] )        -- on the receiver
+ *   grad_x[t]  = bf16( sum over t's rank rows p, ranks ascending, of
+ *                      grad_xr[p] )                       -- on the sender  */
+int oracle_dispatch_backward(const oracle_dims* d, const int32_t* fan_dst, const int32_t* tok_rank_row,
+                             int32_t n_rank_rows, const uint16_t* grad_xe, uint16_t* grad_xr, uint16_t* grad_x)
+{
+    int rc = oracle_check_dims(d);
+    if (rc) return rc;
+    const int T = d->num_tokens, k = d->top_k, R = d->num_ranks;
+    const int Epr = d->num_experts / R, KR = imin(k, R), D = imin(k, Epr);
+    const int64_t H = d->hidden;
+    for (int64_t p = 0; p < n_rank_rows; ++p)
+        for (int64_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int i = 0; i < D; ++i) {
+                int64_t q = fan_dst[p * D + i];
+                if (q < 0) break;
+                acc = acc + bf16_to_f32(grad_xe[q * H + h]);
+            }
+            grad_xr[p * H + h] = f32_to_bf16_rne(acc);
+        }
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int i = 0; i < KR; ++i) {
+                int64_t p = tok_rank_row[t * KR + i];
+                if (p < 0) break;
+                acc = acc + bf16_to_f32(grad_xr[p * H + h]);
+            }
+            grad_x[t * H + h] = f32_to_bf16_rne(acc);
+        }
+    return OR_OK;
+}
+
+/* Backward of combine, out[t] = sum_j w[t][j] * ye[comb_row[t][j]]:
+ *   grad_ye[comb_row[t][j]] = bf16( w[t][j] * grad_out[t] )   (fp32 product)
+ *   grad_w[t][j] = sum over h of grad_out[t][h] * ye[comb_row[t][j]][h]
+ * The gate gradient is returned in fp64: each bf16 x bf16 product is exact
+ * in fp64 and the sum keeps 53 bits, so it stands for the exact value. */
+int oracle_combine_backward(const oracle_dims* d, const int32_t* comb_row, const uint16_t* grad_out,
+                            const uint16_t* ye, const float* w, uint16_t* grad_ye, double* grad_w)
+{
+    int rc = oracle_check_dims(d);
+    if (rc) return rc;
+    const int T = d->num_tokens, k = d->top_k;
+    const int64_t H = d->hidden;
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            const int64_t q = comb_row[t * k + j];
+            const float wj = w[t * k + j];
+            double dot = 0.0;
+            for (int64_t h = 0; h < H; ++h) {
+                const float g = bf16_to_f32(grad_out[t * H + h]);
+                const float prod = wj * g;
+                grad_ye[q * H + h] = f32_to_bf16_rne(prod);
+                dot += (double)g * (double)bf16_to_f32(ye[q * H + h]);
+            }
+            grad_w[t * k + j] = dot;
+        }
+    return OR_OK;
+}
+
+/* Combine with one row per (token, rank) on the way back:
+ *   partial[p] = bf16( sum over the expert rows q fed by rank row p, q
+ *                      ascending, of gate(q) * ye[q] )   (fp32 fma chain)
+ *   out[t]     = bf16( sum over t's rank rows p, ranks ascending, of partial[p] )
+ * gate(q) is w[t][j] for the (t, j) with comb_row[t][j] = q. */
+int oracle_combine_rank_partial(const oracle_dims* d, const int32_t* fan_dst, const int32_t* tok_rank_row,
+                                const int32_t* comb_row, int32_t n_rank_rows, const uint16_t* ye, const float* w,
+                                uint16_t* partial, uint16_t* out)
+{
+    int rc = oracle_check_dims(d);
+    if (rc) return rc;
+    const int T = d->num_tokens, k = d->top_k, R = d->num_ranks;
+    const int Epr = d->num_experts / R, KR = imin(k, R), D = imin(k, Epr);
+    const int64_t H = d->hidden, Tk = (int64_t)T * k;
+    float* gate = (float*)malloc(sizeof(float) * (size_t)(Tk > 0 ? Tk : 1));
+    if (!gate) return OR_E_INVALID_ARG;
+    for (int64_t i = 0; i < Tk; ++i) gate[comb_row[i]] = w[i];
+    for (int64_t p = 0; p < n_rank_rows; ++p)
+        for (int64_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int i = 0; i < D; ++i) {
+                int64_t q = fan_dst[p * D + i];
+                if (q < 0) break;
+                acc = fmaf(gate[q], bf16_to_f32(ye[q * H + h]), acc);
+            }
+            partial[p * H + h] = f32_to_bf16_rne(acc);
+        }
+    free(gate);
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int i = 0; i < KR; ++i) {
+                int64_t p = tok_rank_row[t * KR + i];
+                if (p < 0) break;
+                acc = acc + bf16_to_f32(partial[p * H + h]);
+            }
+            out[t * H + h] = f32_to_bf16_rne(acc);
+        }
+    return OR_OK;
+}

@@ -278,3 +278,116 @@ def run_battery(orc) -> None:
     comb_row = np.array([[0, 1], [2, 3]], np.int32)
     w = np.array([[1.0, 1.0], [0.5, 0.25]], np.float32)
     np.testing.assert_array_equal(orc.combine(comb_row, ye, w, 4, 1), combine_exact(comb_row, ye, w))
+
+
+# --------------------------------------------------------------------------
+# backward and rank-partial combine
+# --------------------------------------------------------------------------
+    run_battery_backward(orc)
+
+
+def f32_add_exact(a: float, b: float) -> float:
+    return _round_fraction(Fraction(a) + Fraction(b), 24, -126, 127)
+
+
+def bf16_of_f32_bits(v: float) -> int:
+    return bf16_bits_of_exact(v)
+
+
+def _f(bits):
+    return float((np.uint32(bits) << np.uint32(16)).view(np.float32))
+
+
+def staged_sum_exact(groups, rows_bits):
+    """bf16( fp32 running sum from +0 over rows_bits[g] for g in groups ), per column, exactly."""
+    H = rows_bits.shape[1]
+    out = np.zeros(H, np.uint16)
+    for h in range(H):
+        acc = 0.0
+        for g in groups:
+            acc = f32_add_exact(acc, _f(rows_bits[g, h]))
+        out[h] = bf16_bits_of_exact(acc)
+    return out
+
+
+def check_dispatch_backward_exact(plan, grad_xe, gxr, gx):
+    """Exact replay of both stages with rationals (tiny inputs)."""
+    N = plan["N"]
+    for p in range(N):
+        qs = [int(q) for q in plan["fan_dst"][p] if q >= 0]
+        np.testing.assert_array_equal(gxr[p], staged_sum_exact(qs, grad_xe))
+    for t in range(plan["tok_rank_row"].shape[0]):
+        ps = [int(p) for p in plan["tok_rank_row"][t] if p >= 0]
+        np.testing.assert_array_equal(gx[t], staged_sum_exact(ps, gxr))
+
+
+def check_rank_partial_exact(plan, ye, w, part, out):
+    T, k = plan["comb_row"].shape
+    gate = np.zeros(T * k, np.float32)
+    gate[plan["comb_row"].ravel()] = w.ravel()
+    H = ye.shape[1]
+    for p in range(plan["N"]):
+        qs = [int(q) for q in plan["fan_dst"][p] if q >= 0]
+        for h in range(H):
+            acc = 0.0
+            for q in qs:
+                acc = f32_fma_exact(float(gate[q]), _f(ye[q, h]), acc)
+            assert part[p, h] == bf16_bits_of_exact(acc), (p, h)
+    for t in range(T):
+        ps = [int(p) for p in plan["tok_rank_row"][t] if p >= 0]
+        np.testing.assert_array_equal(out[t], staged_sum_exact(ps, part))
+
+
+def order_sensitive_backward_case():
+    """Tiny plans where summation order decides the bf16 result:
+    (a) one token, three experts on one rank: the receiver sums three rows;
+    (b) one token, one expert on each of three ranks: the sender sums three.
+    Row values 1, -1, 2^-30: ascending order keeps 2^-30, any other loses it."""
+    import synth
+    vals = np.array([[1.0] * 8, [-1.0] * 8, [2.0 ** -30] * 8], np.float32)
+    rows = synth.f32_to_bf16_bits(vals)
+    case_a = dict(idx=np.array([[0, 1, 2]], np.int32), E=8, R=1, g=rows)
+    case_b = dict(idx=np.array([[0, 2, 4]], np.int32), E=6, R=3, g=rows)
+    return case_a, case_b
+
+
+def run_battery_backward(orc) -> None:
+    import synth
+    for case in order_sensitive_backward_case():
+        rc, p = orc.plan(case["idx"], 8, case["E"], case["R"])
+        assert rc == 0
+        gxr, gx = orc.dispatch_backward(p, case["g"], 1, case["E"], 3, case["R"])
+        check_dispatch_backward_exact(p, case["g"], gxr, gx)
+        assert float((np.uint32(gx[0, 0]) << np.uint32(16)).view(np.float32)) == 2.0 ** -30
+        w = np.array([[1.0, 1.0, 1.0]], np.float32)
+        part, out = orc.combine_rank_partial(p, case["g"], w, case["E"], case["R"])
+        check_rank_partial_exact(p, case["g"], w, part, out)
+        assert float((np.uint32(out[0, 0]) << np.uint32(16)).view(np.float32)) == 2.0 ** -30
+    for (T, E, k, R) in ((9, 8, 3, 4), (7, 12, 4, 2), (6, 16, 5, 16)):
+        rng = np.random.default_rng(T * 101 + E)
+        idx, w = synth.random_routing(rng, T, E, k, signed_gates=True)
+        rc, p = orc.plan(idx, 8, E, R)
+        ye = synth.wide_bf16(rng, (T * k, 8), -6, 6)
+        gxr, gx = orc.dispatch_backward(p, ye, T, E, k, R)
+        check_dispatch_backward_exact(p, ye, gxr, gx)
+        part, out = orc.combine_rank_partial(p, ye, w, E, R)
+        check_rank_partial_exact(p, ye, w, part, out)
+        g = synth.wide_bf16(rng, (T, 8), -6, 6)
+        gye, gw = orc.combine_backward(p["comb_row"], g, ye, w, E, R)
+        check_combine_backward(p["comb_row"], g, ye, w, gye, gw)
+
+
+def check_combine_backward(comb_row, g, ye, w, gye, gw):
+    """grad_ye[q] = bf16(fp32(w * g)) element by element; grad_w = fp64 dot
+    (numpy) of the bf16 rows."""
+    T, k = comb_row.shape
+    gf = (g.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    yf = (ye.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    for t in range(T):
+        for j in range(k):
+            q = comb_row[t, j]
+            prod = (np.float32(w[t, j]) * gf[t]).astype(np.float32)       # IEEE fp32 products
+            expect = np.array([bf16_bits_of_exact(float(v)) for v in prod], np.uint16)
+            np.testing.assert_array_equal(gye[q], expect)
+            dot = float(np.dot(gf[t].astype(np.float64), yf[q].astype(np.float64)))
+            assert abs(gw[t, j] - dot) <= 1e-12 * max(1.0, float(np.abs(gf[t].astype(np.float64) * yf[q]).sum()))

@@ -36,10 +36,22 @@ MUTANTS = {
                         "acc = acc + w[(int64_t)t * k + j] * bf16_to_f32(ye[q * H + h]);"),
     "combine_wrong_gate_index": ("acc = fmaf(w[(int64_t)t * k + j], bf16_to_f32(ye[q * H + h]), acc);",
                                  "acc = fmaf(w[(int64_t)t * k + (k - 1 - j)], bf16_to_f32(ye[q * H + h]), acc);"),
-    "combine_start_minus_zero": ("float acc = 0.0f;", "float acc = -0.0f;"),
+    "combine_start_minus_zero": ("float acc = 0.0f;\n            for (int j = 0; j < k; ++j) {",
+                                 "float acc = -0.0f;\n            for (int j = 0; j < k; ++j) {"),
     "round_truncate": ("if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;", ""),
     "round_ties_away": ("if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;",
                         "if (rest >= 0x8000u) keep += 1u;"),
+    "dbwd_receiver_descending": ("for (int i = 0; i < D; ++i) {\n                int64_t q = fan_dst[p * D + i];\n                if (q < 0) break;\n                acc = acc + bf16_to_f32(grad_xe[q * H + h]);",
+                                 "for (int i = D - 1; i >= 0; --i) {\n                int64_t q = fan_dst[p * D + i];\n                if (q < 0) continue;\n                acc = acc + bf16_to_f32(grad_xe[q * H + h]);"),
+    "dbwd_sender_skips_first_rank": ("acc = acc + bf16_to_f32(grad_xr[p * H + h]);",
+                                     "acc = i ? acc + bf16_to_f32(grad_xr[p * H + h]) : acc;"),
+    "cbwd_wrong_gate": ("const float wj = w[t * k + j];", "const float wj = w[t * k + (k - 1 - j)];"),
+    "cbwd_dot_drops_last": ("dot += (double)g * (double)bf16_to_f32(ye[q * H + h]);",
+                            "dot += (h + 1 < H) ? (double)g * (double)bf16_to_f32(ye[q * H + h]) : 0.0;"),
+    "partial_gate_by_slot": ("for (int64_t i = 0; i < Tk; ++i) gate[comb_row[i]] = w[i];",
+                             "for (int64_t i = 0; i < Tk; ++i) gate[i] = w[i];"),
+    "partial_truncates": ("partial[p * H + h] = f32_to_bf16_rne(acc);",
+                          "{ uint32_t u_; memcpy(&u_, &acc, 4); partial[p * H + h] = (uint16_t)(u_ >> 16); }"),
     "flush_subnormals": ("uint32_t u = (uint32_t)b << 16;\n    float f;",
                          "uint32_t u = (uint32_t)b << 16;\n    if ((u & 0x7f800000u) == 0) u &= 0x80000000u;\n    float f;"),
 }

@@ -155,6 +155,114 @@ def pmc_summary(args):
     print("\n".join(lines))
 
 
+def path_bytes(path, T, H, k, N):
+    """Algorithmic bytes per kernel of the other paths."""
+    row = 2 * H
+    if path == "backward":
+        # combine backward: grad_out once, ye and grad_ye for every slot, rows+gates in, grad_w out
+        cbwd = row * (T + 2 * T * k) + 12 * T * k
+        # receiver: grad_xe rows in, one row per (token, rank) out; sender: those in, grad_x out
+        recv = row * (T * k + N) + 4 * T * k
+        send = row * (N + T) + 4 * N
+        return {"combine_bwd": cbwd, "sum_expert_rows": recv, "sum_rank_rows": send, "total": cbwd + recv + send}
+    # rank-partial combine: gate scatter, weighted receiver sum, sender sum
+    recv = row * (T * k + N) + 16 * T * k
+    send = row * (N + T) + 4 * N
+    return {"sum_expert_rows": recv, "sum_rank_rows": send, "total": recv + send}
+
+
+def bench_path(args):
+    """--path backward | rank-partial: the training direction (combine
+    backward + dispatch backward, on the forward's plan) or the combine with
+    one row per (token, rank) on the return path."""
+    import numpy as np
+    import torch
+
+    import moe_expert_token_amd as ms
+    import synth
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.config]
+    T, H, E, k, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.R
+    KR = min(k, R)
+    log(f"[bench] {args.path} on {cfg.name}: generating inputs")
+    idx_h, w_h = synth.make_routing(cfg, args.seed)
+    ye_h = synth.make_expert_outputs(cfg, args.seed)
+    rng = np.random.default_rng(args.seed + 7)
+    g16 = lambda a: torch.from_numpy(a.view(np.int16)).to(dev)  # noqa: E731
+    idx, w, ye = torch.from_numpy(idx_h).to(dev), torch.from_numpy(w_h).to(dev), g16(ye_h)
+    dims = ms.dims_of(T, H, E, k, R)
+    ws = torch.empty(ms.moe_shuffle_workspace_size(dims), dtype=torch.uint8, device=dev)
+    plan = ms.moe_shuffle_plan(dims, idx, ws)
+    N = ms.moe_shuffle_plan_query(plan)["N"]
+    rows = torch.empty((T * KR, H), dtype=torch.int16, device=dev)
+    out = torch.empty((T, H), dtype=torch.int16, device=dev)
+    if args.path == "backward":
+        gxe_h = synth.wide_bf16(rng, (T * k, H), -8, 8)
+        gout_h = synth.wide_bf16(rng, (T, H), -8, 8)
+        gxe, gout = g16(gxe_h), g16(gout_h)
+        gye = torch.empty((T * k, H), dtype=torch.int16, device=dev)
+        gw = torch.empty((T * k,), dtype=torch.float32, device=dev)
+        names = ("combine_bwd", "sum_expert_rows", "sum_rank_rows")
+        calls = (lambda: ms.moe_shuffle_combine_backward(plan, gout, ye, w, gye, gw),
+                 lambda: ms.moe_shuffle_sum_expert_rows(plan, gxe, None, rows),
+                 lambda: ms.moe_shuffle_sum_rank_rows(plan, rows, out))
+    else:
+        names = ("sum_expert_rows", "sum_rank_rows")
+        calls = (lambda: ms.moe_shuffle_sum_expert_rows(plan, ye, w, rows),
+                 lambda: ms.moe_shuffle_sum_rank_rows(plan, rows, out))
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        events[i][0].record()
+        for j, c in enumerate(calls):
+            c()
+            events[i][j + 1].record()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    us = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]) * 1e3)
+          for j, n in enumerate(names)}
+    B = path_bytes(args.path, T, H, k, N)
+    parity = None
+    if not args.no_parity:
+        import oracle
+        orc = oracle.get()
+        rc, o = orc.plan(idx_h, H, E, R)
+        if args.path == "backward":
+            o_gxr, o_gx = orc.dispatch_backward(o, gxe_h, T, E, k, R)
+            o_gye, _ = orc.combine_backward(o["comb_row"], gout_h, ye_h, w_h, E, R)
+            parity = {"grad_xr_bitexact": bool(np.array_equal(rows[:N].cpu().numpy().view(np.uint16), o_gxr)),
+                      "grad_x_bitexact": bool(np.array_equal(out.cpu().numpy().view(np.uint16), o_gx)),
+                      "grad_ye_bitexact": bool(np.array_equal(gye.cpu().numpy().view(np.uint16), o_gye))}
+        else:
+            o_part, o_out = orc.combine_rank_partial(o, ye_h, w_h, E, R)
+            parity = {"partial_bitexact": bool(np.array_equal(rows[:N].cpu().numpy().view(np.uint16), o_part)),
+                      "out_bitexact": bool(np.array_equal(out.cpu().numpy().view(np.uint16), o_out))}
+        log(f"[bench] parity vs oracle: {parity}")
+    dom = max(names, key=lambda n: B[n])
+    value = B["total"] / (ms_per_step * 1e-3) / 1e9
+    rec = {
+        "metric": f"{args.path} shuffle effective HBM GB/s (fraction of peak), 1 GPU", "value": round(value, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "H": H, "E": E, "k": k, "R": R, "N": N, "path": args.path},
+        "frac_of_peak": round(value / PEAK_HBM_GBPS, 4), "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "kernel_us": {n: round(us[n], 2) for n in names}, "algorithmic_bytes": B, "accumulate": "fp32",
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(B[dom] / (us[dom] * 1e-6) / 1e9, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(B[dom] / (us[dom] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "alg_bytes_per_launch": B[dom], "avg_launch_us": round(us[dom], 2)},
+        "cpu_baseline": None, "parity": parity, "kernel_src_sha256_16": source_digest(),
+    }
+    ms.moe_shuffle_plan_destroy(plan)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +273,9 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=12.0, help="CPU-oracle timing budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--path", default="forward", choices=("forward", "backward", "rank-partial"),
+                    help="forward (default): plan + dispatch + combine; backward: combine and dispatch backward; "
+                         "rank-partial: combine through one row per (token, rank)")
     ap.add_argument("--pmc-summary", action="store_true", help="summarise rocprofv3 CSVs into profiles/ (no GPU)")
     ap.add_argument("--fetch-csv")
     ap.add_argument("--write-csv")
@@ -196,6 +307,9 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda:0")
+    if args.path != "forward":
+        bench_path(args)
+        return
 
     cfg = synth.CONFIGS[args.config]
     T, H, E, k, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.R

@@ -172,6 +172,60 @@ int moe_shuffle_dispatch_fanout(moe_shuffle_plan_t plan, const void* xr, int64_t
 int moe_shuffle_combine(moe_shuffle_plan_t plan, const void* ye, const float* topk_w, void* out,
                         void* stream);
 
+/*
+ * The return path with one row per (token, rank) pair, and the training
+ * direction.  The FUSCO abstract reports training latency, so the shuffle
+ * also runs backwards; the DySHARP write-up (section 2 / Fig. 1) notes that
+ * the results of a token's experts on one device can be summed before they
+ * travel back, which is the send-once rule applied to the return path.
+ * Arithmetic: fp32 accumulator from +0, terms in the stated order, one
+ * round-to-nearest-even to bf16 per stored row; rows exchanged between ranks
+ * are bf16.
+ */
+
+/* Receiver side:  rank_rows[p] = bf16( sum over the expert rows q that rank
+ * row p fed (fan_dst[p], ascending q) of g(q) * expert_rows[q] ), p < N, with
+ * g(q) = topk_w[t][j] for comb_row[t][j] = q, or g = 1 when topk_w is NULL.
+ *   expert_rows  device bf16 [T*k, H] (expert-major)
+ *   topk_w       device fp32 [T, k] or NULL
+ *   rank_rows    device bf16 [rank_rows_cap, H]; rows [0, N) are written;
+ *                rank_rows_cap as for xr in moe_shuffle_dispatch.
+ * Uses the plan workspace for the gates of the expert rows. */
+int moe_shuffle_sum_expert_rows(moe_shuffle_plan_t plan, const void* expert_rows, const float* topk_w,
+                                void* rank_rows, int64_t rank_rows_cap, void* stream);
+
+/* Sender side:  out[t] = bf16( sum over t's rank rows p (tok_rank_row[t],
+ * ranks ascending) of rank_rows[p] ), t < T.
+ *   rank_rows  device bf16 [rank_rows_cap, H] (rows [0, N) are read)
+ *   out        device bf16 [T, H]; must not overlap rank_rows. */
+int moe_shuffle_sum_rank_rows(moe_shuffle_plan_t plan, const void* rank_rows, int64_t rank_rows_cap, void* out,
+                              void* stream);
+
+/* Backward of dispatch (the adjoint of the two copies): grad_xr = the
+ * receiver's unweighted sum of grad_xe, then grad_x = the sender's sum of
+ * grad_xr.  grad_xe [T*k, H], grad_xr [grad_xr_rows, H], grad_x [T, H],
+ * all bf16, pairwise disjoint. */
+int moe_shuffle_dispatch_backward(moe_shuffle_plan_t plan, const void* grad_xe, void* grad_xr,
+                                  int64_t grad_xr_rows, void* grad_x, void* stream);
+
+/* Combine through per-(token, rank) partial rows: partial = the receiver's
+ * gate-weighted sum of ye, out = the sender's sum of partial.  The return
+ * path carries N rows instead of T*k.  ye [T*k, H], partial [partial_rows, H],
+ * out [T, H] bf16, pairwise disjoint; topk_w fp32 [T, k]. */
+int moe_shuffle_combine_rank_partial(moe_shuffle_plan_t plan, const void* ye, const float* topk_w, void* partial,
+                                     int64_t partial_rows, void* out, void* stream);
+
+/* Backward of combine, out[t] = sum_j w[t][j] * ye[comb_row[t][j]]:
+ *   grad_ye[comb_row[t][j]] = bf16( fp32(w[t][j] * grad_out[t]) )
+ *   grad_w[t][j] = sum over h of grad_out[t][h] * ye[comb_row[t][j]][h] in fp32:
+ *     each lane sums its elements in ascending h, a butterfly adds the 64
+ *     lanes, then the 512-element chunks of the row are added in order.
+ *   grad_out [T, H], ye [T*k, H], grad_ye [T*k, H] bf16; topk_w, grad_w fp32
+ *   [T, k].  grad_ye must not overlap ye or grad_out.  Uses the plan
+ *   workspace for the per-chunk partial sums. */
+int moe_shuffle_combine_backward(moe_shuffle_plan_t plan, const void* grad_out, const void* ye, const float* topk_w,
+                                 void* grad_ye, float* grad_w, void* stream);
+
 /* Synchronises `stream`, reads N and the status word back to the host.
  * Returns the plan's status (MOE_SHUFFLE_OK or MOE_SHUFFLE_E_BAD_INDEX). */
 int moe_shuffle_plan_query(moe_shuffle_plan_t plan, void* stream, moe_shuffle_plan_info* info);

@@ -23,7 +23,8 @@ EXPORTS = (
     "moe_shuffle_workspace_size", "moe_shuffle_plan", "moe_shuffle_dispatch", "moe_shuffle_dispatch_send",
     "moe_shuffle_dispatch_fanout", "moe_shuffle_combine", "moe_shuffle_plan_query",
     "moe_shuffle_plan_arrays_get", "moe_shuffle_plan_destroy", "moe_shuffle_strerror",
-    "moe_shuffle_last_hip_error",
+    "moe_shuffle_last_hip_error", "moe_shuffle_sum_expert_rows", "moe_shuffle_sum_rank_rows",
+    "moe_shuffle_dispatch_backward", "moe_shuffle_combine_rank_partial", "moe_shuffle_combine_backward",
 )
 
 
@@ -80,6 +81,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_shuffle_plan_destroy": (None, [_vp]),
         "moe_shuffle_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_shuffle_last_hip_error": (ctypes.c_int, []),
+        "moe_shuffle_sum_expert_rows": (ctypes.c_int, [_vp, _vp, _vp, _vp, i64, _vp]),
+        "moe_shuffle_sum_rank_rows": (ctypes.c_int, [_vp, _vp, i64, _vp, _vp]),
+        "moe_shuffle_dispatch_backward": (ctypes.c_int, [_vp, _vp, _vp, i64, _vp, _vp]),
+        "moe_shuffle_combine_rank_partial": (ctypes.c_int, [_vp, _vp, _vp, _vp, i64, _vp, _vp]),
+        "moe_shuffle_combine_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -176,6 +182,31 @@ def moe_shuffle_dispatch_fanout(plan: Plan, xr, xe, stream=None):
 def moe_shuffle_combine(plan: Plan, ye, topk_w, out, stream=None):
     _check("moe_shuffle_combine", load().moe_shuffle_combine(plan.handle, _ptr(ye), _ptr(topk_w), _ptr(out),
                                                              _stream(stream)))
+
+
+def moe_shuffle_sum_expert_rows(plan: Plan, expert_rows, topk_w, rank_rows, stream=None):
+    _check("moe_shuffle_sum_expert_rows", load().moe_shuffle_sum_expert_rows(
+        plan.handle, _ptr(expert_rows), _ptr(topk_w), _ptr(rank_rows), rank_rows.shape[0], _stream(stream)))
+
+
+def moe_shuffle_sum_rank_rows(plan: Plan, rank_rows, out, stream=None):
+    _check("moe_shuffle_sum_rank_rows", load().moe_shuffle_sum_rank_rows(
+        plan.handle, _ptr(rank_rows), rank_rows.shape[0], _ptr(out), _stream(stream)))
+
+
+def moe_shuffle_dispatch_backward(plan: Plan, grad_xe, grad_xr, grad_x, stream=None):
+    _check("moe_shuffle_dispatch_backward", load().moe_shuffle_dispatch_backward(
+        plan.handle, _ptr(grad_xe), _ptr(grad_xr), grad_xr.shape[0], _ptr(grad_x), _stream(stream)))
+
+
+def moe_shuffle_combine_rank_partial(plan: Plan, ye, topk_w, partial, out, stream=None):
+    _check("moe_shuffle_combine_rank_partial", load().moe_shuffle_combine_rank_partial(
+        plan.handle, _ptr(ye), _ptr(topk_w), _ptr(partial), partial.shape[0], _ptr(out), _stream(stream)))
+
+
+def moe_shuffle_combine_backward(plan: Plan, grad_out, ye, topk_w, grad_ye, grad_w, stream=None):
+    _check("moe_shuffle_combine_backward", load().moe_shuffle_combine_backward(
+        plan.handle, _ptr(grad_out), _ptr(ye), _ptr(topk_w), _ptr(grad_ye), _ptr(grad_w), _stream(stream)))
 
 
 def moe_shuffle_plan_query(plan: Plan, stream=None) -> dict:

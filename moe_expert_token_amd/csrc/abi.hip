@@ -93,6 +93,8 @@ void make_layout(const moe_shuffle_dims& d, Layout& L)
     L.tile_hist = take(i4 * (size_t)(L.C + 1) * L.ntiles);
     L.tile_base = take(i4 * (size_t)L.C * L.ntiles);
     L.col_total = take(i4 * L.C);
+    L.gate_of_row = take(i4 * T * k);
+    L.bwd_dots = take(i4 * T * (size_t)((L.H / 8 + kWave - 1) / kWave) * k);
     L.total = o;
 }
 
@@ -253,6 +255,106 @@ int moe_shuffle_combine(moe_shuffle_plan_t plan, const void* ye, const float* to
     if (overlap(ye, row * (size_t)L.T * L.k, out, row * L.T)) return MOE_SHUFFLE_E_INVALID_ARG;
     const hipError_t e = ms::launch_combine_rows(ye, topk_w, at<int32_t>(plan, L.comb_row), out, L.T, L.k, L.H,
                                                  at<int32_t>(plan, L.status), (hipStream_t)stream);
+    return e == hipSuccess ? MOE_SHUFFLE_OK : hip_fail(e);
+}
+
+int moe_shuffle_sum_expert_rows(moe_shuffle_plan_t plan, const void* expert_rows, const float* topk_w,
+                                void* rank_rows, int64_t rank_rows_cap, void* stream)
+{
+    int rc = check_plan(plan);
+    if (rc) return rc;
+    const ms::Layout& L = plan->L;
+    if (L.T == 0) return MOE_SHUFFLE_OK;
+    if (!expert_rows || !rank_rows) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (misaligned(expert_rows, 16) || misaligned(rank_rows, 16) || misaligned(topk_w, 4)) return MOE_SHUFFLE_E_ALIGN;
+    const int64_t need = rank_rows_needed(plan);
+    if (rank_rows_cap < need) return MOE_SHUFFLE_E_INVALID_ARG;
+    const size_t row = (size_t)L.H * 2;
+    if (overlap(expert_rows, row * (size_t)L.T * L.k, rank_rows, row * (size_t)rank_rows_cap))
+        return MOE_SHUFFLE_E_INVALID_ARG;
+    const hipError_t e = ms::launch_sum_expert_rows(
+        expert_rows, (int64_t)L.T * L.k, topk_w, at<int32_t>(plan, L.comb_row), at<float>(plan, L.gate_of_row),
+        at<int32_t>(plan, L.fan_dst), L.D, rank_rows, need, at<int32_t>(plan, L.n_rank_rows), L.H,
+        at<int32_t>(plan, L.status), (hipStream_t)stream);
+    return e == hipSuccess ? MOE_SHUFFLE_OK : hip_fail(e);
+}
+
+int moe_shuffle_sum_rank_rows(moe_shuffle_plan_t plan, const void* rank_rows, int64_t rank_rows_cap, void* out,
+                              void* stream)
+{
+    int rc = check_plan(plan);
+    if (rc) return rc;
+    const ms::Layout& L = plan->L;
+    if (L.T == 0) return MOE_SHUFFLE_OK;
+    if (!rank_rows || !out) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (misaligned(rank_rows, 16) || misaligned(out, 16)) return MOE_SHUFFLE_E_ALIGN;
+    if (rank_rows_cap < rank_rows_needed(plan)) return MOE_SHUFFLE_E_INVALID_ARG;
+    const size_t row = (size_t)L.H * 2;
+    if (overlap(rank_rows, row * (size_t)rank_rows_cap, out, row * L.T)) return MOE_SHUFFLE_E_INVALID_ARG;
+    const hipError_t e = ms::launch_sum_rank_rows(rank_rows, rank_rows_cap, at<int32_t>(plan, L.tok_rank_row), L.KR,
+                                                  out, L.T, L.H, at<int32_t>(plan, L.status), (hipStream_t)stream);
+    return e == hipSuccess ? MOE_SHUFFLE_OK : hip_fail(e);
+}
+
+int moe_shuffle_dispatch_backward(moe_shuffle_plan_t plan, const void* grad_xe, void* grad_xr, int64_t grad_xr_rows,
+                                  void* grad_x, void* stream)
+{
+    int rc = check_plan(plan);
+    if (rc) return rc;
+    const ms::Layout& L = plan->L;
+    if (L.T == 0) return MOE_SHUFFLE_OK;
+    if (!grad_xe || !grad_xr || !grad_x) return MOE_SHUFFLE_E_INVALID_ARG;
+    const size_t row = (size_t)L.H * 2;
+    if (overlap(grad_xe, row * (size_t)L.T * L.k, grad_x, row * L.T)) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (misaligned(grad_x, 16) || misaligned(grad_xr, 16) || misaligned(grad_xe, 16)) return MOE_SHUFFLE_E_ALIGN;
+    if (grad_xr_rows < rank_rows_needed(plan)) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (overlap(grad_xr, row * (size_t)grad_xr_rows, grad_x, row * L.T) ||
+        overlap(grad_xe, row * (size_t)L.T * L.k, grad_xr, row * (size_t)grad_xr_rows))
+        return MOE_SHUFFLE_E_INVALID_ARG;
+    rc = moe_shuffle_sum_expert_rows(plan, grad_xe, nullptr, grad_xr, grad_xr_rows, stream);
+    if (rc) return rc;
+    return moe_shuffle_sum_rank_rows(plan, grad_xr, grad_xr_rows, grad_x, stream);
+}
+
+int moe_shuffle_combine_rank_partial(moe_shuffle_plan_t plan, const void* ye, const float* topk_w, void* partial,
+                                     int64_t partial_rows, void* out, void* stream)
+{
+    int rc = check_plan(plan);
+    if (rc) return rc;
+    const ms::Layout& L = plan->L;
+    if (L.T == 0) return MOE_SHUFFLE_OK;
+    if (!ye || !topk_w || !partial || !out) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (misaligned(ye, 16) || misaligned(partial, 16) || misaligned(out, 16) || misaligned(topk_w, 4))
+        return MOE_SHUFFLE_E_ALIGN;
+    if (partial_rows < rank_rows_needed(plan)) return MOE_SHUFFLE_E_INVALID_ARG;
+    const size_t row = (size_t)L.H * 2;
+    if (overlap(ye, row * (size_t)L.T * L.k, out, row * L.T) ||
+        overlap(ye, row * (size_t)L.T * L.k, partial, row * (size_t)partial_rows) ||
+        overlap(partial, row * (size_t)partial_rows, out, row * L.T))
+        return MOE_SHUFFLE_E_INVALID_ARG;
+    rc = moe_shuffle_sum_expert_rows(plan, ye, topk_w, partial, partial_rows, stream);
+    if (rc) return rc;
+    return moe_shuffle_sum_rank_rows(plan, partial, partial_rows, out, stream);
+}
+
+int moe_shuffle_combine_backward(moe_shuffle_plan_t plan, const void* grad_out, const void* ye, const float* topk_w,
+                                 void* grad_ye, float* grad_w, void* stream)
+{
+    int rc = check_plan(plan);
+    if (rc) return rc;
+    const ms::Layout& L = plan->L;
+    if (L.T == 0) return MOE_SHUFFLE_OK;
+    if (!grad_out || !ye || !topk_w || !grad_ye || !grad_w) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (misaligned(grad_out, 16) || misaligned(ye, 16) || misaligned(grad_ye, 16) || misaligned(topk_w, 4) ||
+        misaligned(grad_w, 4))
+        return MOE_SHUFFLE_E_ALIGN;
+    const size_t row = (size_t)L.H * 2, erows = row * (size_t)L.T * L.k;
+    if (overlap(grad_ye, erows, ye, erows) || overlap(grad_ye, erows, grad_out, row * L.T) ||
+        overlap(grad_w, sizeof(float) * (size_t)L.T * L.k, grad_ye, erows))
+        return MOE_SHUFFLE_E_INVALID_ARG;
+    const hipError_t e = ms::launch_combine_backward(grad_out, ye, topk_w, at<int32_t>(plan, L.comb_row), grad_ye,
+                                                     grad_w, at<float>(plan, L.bwd_dots), L.T, L.k, L.H,
+                                                     at<int32_t>(plan, L.status), (hipStream_t)stream);
     return e == hipSuccess ? MOE_SHUFFLE_OK : hip_fail(e);
 }
 

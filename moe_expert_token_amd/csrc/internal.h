@@ -26,6 +26,8 @@ struct Layout {
     size_t send_token, tok_rank_row, fan_src, fan_dst, comb_row;
     size_t rank_segs, expert_segs;
     size_t tile_hist, tile_base, col_total;
+    size_t gate_of_row;  // fp32 [T*k]: the gate of every expert row (rank-partial combine)
+    size_t bwd_dots;     // fp32 [T][ceil(H/512)][k]: gate-gradient partial sums
     size_t total;
 };
 
@@ -55,5 +57,20 @@ hipError_t launch_fanout_rows(bool send, const void* src, void* dst, const int32
 // out[t] = bf16( fp32 fma chain over j of w[t][j] * ye[rows[t][j]] ).
 hipError_t launch_combine_rows(const void* ye, const float* w, const int32_t* rows, void* out,
                                int T, int k, int H, const int32_t* status, hipStream_t s);
+
+// out[p] = bf16( sum over q in fan_dst[p] of (gate(q) *) src[q] ) for p < n;
+// gate(q) is scattered from w through comb_row first when w is non-null.
+hipError_t launch_sum_expert_rows(const void* src, int64_t src_rows, const float* w, const int32_t* comb_row,
+                                  float* gate_of_row, const int32_t* fan_dst, int D, void* out, int64_t n_bound,
+                                  const int32_t* n_dev, int H, const int32_t* status, hipStream_t s);
+
+// out[t] = bf16( sum over p in tok_rank_row[t] of src[p] ) for t < T.
+hipError_t launch_sum_rank_rows(const void* src, int64_t src_rows, const int32_t* tok_rank_row, int KR, void* out,
+                                int T, int H, const int32_t* status, hipStream_t s);
+
+// grad_ye[q(t,j)] = bf16(w[t][j] * grad_out[t]); grad_w[t][j] = <grad_out[t], ye[q(t,j)]>.
+hipError_t launch_combine_backward(const void* grad_out, const void* ye, const float* w, const int32_t* comb_row,
+                                   void* grad_ye, float* grad_w, float* dots, int T, int k, int H,
+                                   const int32_t* status, hipStream_t s);
 
 }  // namespace ms

@@ -563,7 +563,17 @@ hipError_t launch_fanout_rows(bool send, const void* src, void* dst, const int32
     }
 }
 
-// ---------------------------------------------------------------- combine
+// ---------------------------------------------------------------- reductions
+//
+// One gather-reduce body serves every "k rows in, one row out" step:
+//   combine                 out[t]  = sum_j  w[t][j] * ye[comb_row[t][j]]
+//   sum of expert rows      rr[p]   = sum_q  (gate(q) *) src[q], q in fan_dst[p]
+//                           (receiver side: dispatch backward, rank-partial combine)
+//   sum of rank rows        out[t]  = sum_p  src[p], p in tok_rank_row[t]
+//                           (sender side of the same two)
+// fp32 accumulator from +0, one fused multiply-add per term in map order
+// (weight 1 for an unweighted sum, where fma(1, x, acc) is exactly x + acc),
+// one round-to-nearest-even to bf16.  A -1 entry ends a map row.
 
 // fp32 -> bf16 bits, round to nearest even; NaN -> quiet NaN of the same sign.
 __device__ __forceinline__ unsigned bf16_rne(float f)
@@ -573,13 +583,218 @@ __device__ __forceinline__ unsigned bf16_rne(float f)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int U, bool FULL>
-__global__ __launch_bounds__(kBlock) void combine_rows_kernel(const u32x4* __restrict__ ye, const float* __restrict__ w,
-                                                              const int32_t* __restrict__ rows_map,
-                                                              u32x4* __restrict__ out, int T, int k, RowSplit rs,
-                                                              const int32_t* __restrict__ status)
+enum WeightMode { kUnweighted = 0, kPerSlot = 1, kPerSourceRow = 2 };
+
+template <int U, bool FULL, int WMODE, bool NTL, bool NTS>
+__device__ __forceinline__ void reduce_rows(int* s_tile, const u32x4* __restrict__ src,
+                                            const int32_t* __restrict__ map, int width,
+                                            const float* __restrict__ w, u32x4* __restrict__ out, int64_t n_bound,
+                                            const int32_t* __restrict__ n_dev, RowSplit rs,
+                                            const int32_t* __restrict__ status)
 {
-    extern __shared__ int s_tile[];  // [rows of this block][k] expert rows, then the same for the gates
+    if (status[0] != MOE_SHUFFLE_OK) return;
+    const int64_t n = n_dev ? (int64_t)n_dev[0] : n_bound;
+    int first, count;
+    block_rows(n, rs, &first, &count);
+    if (count <= 0) return;
+    int* s_rows = s_tile;                               // [rows of this block][width]
+    int* s_w = s_tile + kWavesPerBlock * width;         // per-slot gates, same shape
+    for (int i = threadIdx.x; i < count * width; i += kBlock) {
+        s_rows[i] = map[(int64_t)first * width + i];
+        if (WMODE == kPerSlot) s_w[i] = __float_as_int(w[(int64_t)first * width + i]);
+    }
+    __syncthreads();
+
+    const int wave = wave_id(), lane = lane_id();
+    const int u = (int)blockIdx.x * kWavesPerBlock + wave;
+    const int row = fdiv(u, rs.div);
+    if (row >= n) return;
+    const int V = rs.V;
+    const int c0 = (u - row * rs.cpr) * (kWave * U);
+    const int* trow = s_rows + (row - first) * width;
+    const int* tw = s_w + (row - first) * width;
+
+    float acc[U][8];
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
+    for (int j = 0; j < width; ++j) {
+        const int q = __builtin_amdgcn_readfirstlane(trow[j]);
+        if (q < 0) break;
+        float wj = 1.0f;
+        if (WMODE == kPerSlot) wj = __int_as_float(__builtin_amdgcn_readfirstlane(tw[j]));
+        if (WMODE == kPerSourceRow) wj = w[q];
+        const u32x4* y = src + (int64_t)q * V + c0;
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            if (FULL || c0 + i * kWave + lane < V) {
+                const u32x4 v = load_row16<NTL>(y + i * kWave + lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[i][2 * e] = __builtin_fmaf(wj, __uint_as_float(v[e] << 16), acc[i][2 * e]);
+                    acc[i][2 * e + 1] = __builtin_fmaf(wj, __uint_as_float(v[e] & 0xffff0000u), acc[i][2 * e + 1]);
+                }
+            }
+        }
+    }
+    u32x4* o = out + (int64_t)row * V + c0;
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        if (FULL || c0 + i * kWave + lane < V) {
+            u32x4 pk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pk[e] = bf16_rne(acc[i][2 * e]) | (bf16_rne(acc[i][2 * e + 1]) << 16);
+            store_row16<NTS>(pk, o + i * kWave + lane);
+        }
+    }
+}
+
+#define MS_REDUCE_KERNEL(NAME, NTL, NTS)                                                                         \
+    template <int U, bool FULL, int WMODE>                                                                       \
+    __global__ __launch_bounds__(kBlock) void NAME(const u32x4* __restrict__ src, const int32_t* __restrict__ map, \
+                                                   int width, const float* __restrict__ w, u32x4* __restrict__ out, \
+                                                   int64_t n_bound, const int32_t* __restrict__ n_dev, RowSplit rs, \
+                                                   const int32_t* __restrict__ status)                            \
+    {                                                                                                            \
+        extern __shared__ int s_tile[];                                                                          \
+        reduce_rows<U, FULL, WMODE, NTL, NTS>(s_tile, src, map, width, w, out, n_bound, n_dev, rs, status);      \
+    }
+// ye (expert-major) -> out (token-major): the forward combine.
+MS_REDUCE_KERNEL(combine_rows_kernel, MS_COMBINE_NT_LOAD, MS_COMBINE_NT_STORE)
+// expert-major rows -> one row per (token, rank): the receiver's sum.
+MS_REDUCE_KERNEL(sum_expert_rows_kernel, MS_COMBINE_NT_LOAD, MS_COMBINE_NT_STORE)
+// rank-major rows -> one row per token: the sender's sum.
+MS_REDUCE_KERNEL(sum_rank_rows_kernel, MS_COMBINE_NT_LOAD, MS_COMBINE_NT_STORE)
+#undef MS_REDUCE_KERNEL
+
+// Gathers from a large buffer use whole-row units: past a few GiB of
+// source rows, 8 KiB units measured faster than 1 KiB units on the MI355X
+// (65536 tokens x 8 x 8 KiB combine: 0.80 ms against 0.94 ms); below it 1 KiB
+// units were as fast or faster.
+#ifndef MS_COMBINE_UNIT_LARGE
+#define MS_COMBINE_UNIT_LARGE 8
+#endif
+#ifndef MS_COMBINE_LARGE_BYTES
+#define MS_COMBINE_LARGE_BYTES (2ll << 30)
+#endif
+
+static int reduce_unit(int V, int64_t src_bytes)
+{
+    return fit_unit(V, src_bytes > (int64_t)MS_COMBINE_LARGE_BYTES ? MS_COMBINE_UNIT_LARGE : MS_COMBINE_UNIT);
+}
+
+enum ReduceKind { kCombine = 0, kSumExpertRows = 1, kSumRankRows = 2 };
+
+template <int KIND, int U, bool FULL, int WMODE>
+static void launch_reduce_kernel(dim3 grid, size_t lds, hipStream_t s, const u32x4* src, const int32_t* map,
+                                 int width, const float* w, u32x4* out, int64_t n_bound, const int32_t* n_dev,
+                                 RowSplit rs, const int32_t* status)
+{
+    if (KIND == kCombine)
+        hipLaunchKernelGGL((combine_rows_kernel<U, FULL, WMODE>), grid, dim3(kBlock), lds, s, src, map, width, w, out,
+                           n_bound, n_dev, rs, status);
+    else if (KIND == kSumExpertRows)
+        hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE>), grid, dim3(kBlock), lds, s, src, map, width, w,
+                           out, n_bound, n_dev, rs, status);
+    else
+        hipLaunchKernelGGL((sum_rank_rows_kernel<U, FULL, WMODE>), grid, dim3(kBlock), lds, s, src, map, width, w,
+                           out, n_bound, n_dev, rs, status);
+}
+
+template <int KIND, int WMODE, int U>
+static hipError_t launch_reduce_u(const void* src, const int32_t* map, int width, const float* w, void* out,
+                                  int64_t n_bound, const int32_t* n_dev, int V, const int32_t* status, hipStream_t s)
+{
+    RowSplit rs;
+    if (!make_split(V, U, n_bound, &rs)) return hipErrorInvalidValue;
+    const int64_t units = n_bound * rs.cpr;
+    const dim3 grid((unsigned)((units + kWavesPerBlock - 1) / kWavesPerBlock));
+    const size_t lds = tile_lds_bytes(width, 2);
+    const u32x4* sp = (const u32x4*)src;
+    u32x4* op = (u32x4*)out;
+    if (V % (kWave * U) == 0)
+        launch_reduce_kernel<KIND, U, true, WMODE>(grid, lds, s, sp, map, width, w, op, n_bound, n_dev, rs, status);
+    else
+        launch_reduce_kernel<KIND, U, false, WMODE>(grid, lds, s, sp, map, width, w, op, n_bound, n_dev, rs, status);
+    return hipGetLastError();
+}
+
+template <int KIND, int WMODE>
+static hipError_t launch_reduce(const void* src, int64_t src_rows, const int32_t* map, int width, const float* w,
+                                void* out, int64_t n_bound, const int32_t* n_dev, int H, const int32_t* status,
+                                hipStream_t s)
+{
+    if (n_bound <= 0) return hipSuccess;
+    const int V = H / 8;
+    switch (reduce_unit(V, src_rows * (int64_t)H * 2)) {
+        case 1: return launch_reduce_u<KIND, WMODE, 1>(src, map, width, w, out, n_bound, n_dev, V, status, s);
+        case 2: return launch_reduce_u<KIND, WMODE, 2>(src, map, width, w, out, n_bound, n_dev, V, status, s);
+        case 4: return launch_reduce_u<KIND, WMODE, 4>(src, map, width, w, out, n_bound, n_dev, V, status, s);
+        default: return launch_reduce_u<KIND, WMODE, 8>(src, map, width, w, out, n_bound, n_dev, V, status, s);
+    }
+}
+
+hipError_t launch_combine_rows(const void* ye, const float* w, const int32_t* rows, void* out, int T, int k, int H,
+                               const int32_t* status, hipStream_t s)
+{
+    return launch_reduce<kCombine, kPerSlot>(ye, (int64_t)T * k, rows, k, w, out, T, nullptr, H, status, s);
+}
+
+// gate_of_row[comb_row[t][j]] = w[t][j]: the gate each expert row carries.
+__global__ __launch_bounds__(kBlock) void gate_of_row_kernel(const float* __restrict__ w,
+                                                             const int32_t* __restrict__ comb_row, int64_t n,
+                                                             float* __restrict__ gate_of_row,
+                                                             const int32_t* __restrict__ status)
+{
+    if (status[0] != MOE_SHUFFLE_OK) return;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i < n) gate_of_row[comb_row[i]] = w[i];
+}
+
+hipError_t launch_sum_expert_rows(const void* src, int64_t src_rows, const float* w, const int32_t* comb_row,
+                                  float* gate_of_row, const int32_t* fan_dst, int D, void* out, int64_t n_bound,
+                                  const int32_t* n_dev, int H, const int32_t* status, hipStream_t s)
+{
+    if (n_bound <= 0) return hipSuccess;
+    if (!w) return launch_reduce<kSumExpertRows, kUnweighted>(src, src_rows, fan_dst, D, nullptr, out, n_bound,
+                                                              n_dev, H, status, s);
+    hipLaunchKernelGGL(gate_of_row_kernel, dim3((unsigned)((src_rows + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, w,
+                       comb_row, src_rows, gate_of_row, status);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_reduce<kSumExpertRows, kPerSourceRow>(src, src_rows, fan_dst, D, gate_of_row, out, n_bound, n_dev,
+                                                        H, status, s);
+}
+
+hipError_t launch_sum_rank_rows(const void* src, int64_t src_rows, const int32_t* tok_rank_row, int KR, void* out,
+                                int T, int H, const int32_t* status, hipStream_t s)
+{
+    return launch_reduce<kSumRankRows, kUnweighted>(src, src_rows, tok_rank_row, KR, nullptr, out, T, nullptr, H,
+                                                    status, s);
+}
+
+// ---------------------------------------------------------------- combine backward
+//
+// For out[t] = sum_j w[t][j] * ye[q(t,j)]:
+//   grad_ye[q(t,j)] = bf16( w[t][j] * grad_out[t] )        (one fp32 product)
+//   grad_w[t][j]    = sum_h grad_out[t][h] * ye[q(t,j)][h]
+// One wave per 64*U-vector chunk of a token's row: the chunk of grad_out is
+// loaded once and reused for all k slots.  The gate gradient is summed in a
+// fixed order: each lane over its elements (ascending h), a butterfly over
+// the 64 lanes, then (second kernel) the chunks of a row in ascending order.
+// Each bf16 x bf16 product is exact in fp32.
+
+template <int U, bool FULL>
+__global__ __launch_bounds__(kBlock) void combine_bwd_kernel(const u32x4* __restrict__ grad_out,
+                                                             const u32x4* __restrict__ ye,
+                                                             const float* __restrict__ w,
+                                                             const int32_t* __restrict__ comb_row,
+                                                             u32x4* __restrict__ grad_ye, float* __restrict__ dots,
+                                                             int T, int k, RowSplit rs,
+                                                             const int32_t* __restrict__ status)
+{
+    extern __shared__ int s_tile[];
     if (status[0] != MOE_SHUFFLE_OK) return;
     int first, count;
     block_rows(T, rs, &first, &count);
@@ -587,7 +802,7 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(const u32x4* __res
     int* s_rows = s_tile;
     int* s_w = s_tile + kWavesPerBlock * k;
     for (int i = threadIdx.x; i < count * k; i += kBlock) {
-        s_rows[i] = rows_map[(int64_t)first * k + i];
+        s_rows[i] = comb_row[(int64_t)first * k + i];
         s_w[i] = __float_as_int(w[(int64_t)first * k + i]);
     }
     __syncthreads();
@@ -597,86 +812,99 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(const u32x4* __res
     const int t = fdiv(u, rs.div);
     if (t >= T) return;
     const int V = rs.V;
-    const int c0 = (u - t * rs.cpr) * (kWave * U);
+    const int chunk = u - t * rs.cpr;
+    const int c0 = chunk * (kWave * U);
     const int* trow = s_rows + (t - first) * k;
     const int* tw = s_w + (t - first) * k;
 
-    float acc[U][8];
+    float g[U][8];
+    const u32x4* gp = grad_out + (int64_t)t * V + c0;
 #pragma unroll
-    for (int i = 0; i < U; ++i)
+    for (int i = 0; i < U; ++i) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (FULL || c0 + i * kWave + lane < V) v = load_row16<MS_COMBINE_NT_LOAD>(gp + i * kWave + lane);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
+        for (int e = 0; e < 4; ++e) {
+            g[i][2 * e] = __uint_as_float(v[e] << 16);
+            g[i][2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+        }
+    }
+    float mine = 0.0f;  // lane j keeps slot j's chunk total
     for (int j = 0; j < k; ++j) {
         const int q = __builtin_amdgcn_readfirstlane(trow[j]);
         const float wj = __int_as_float(__builtin_amdgcn_readfirstlane(tw[j]));
         const u32x4* y = ye + (int64_t)q * V + c0;
+        u32x4* gy = grad_ye + (int64_t)q * V + c0;
+        float part = 0.0f;
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             if (FULL || c0 + i * kWave + lane < V) {
                 const u32x4 v = load_row16<MS_COMBINE_NT_LOAD>(y + i * kWave + lane);
+                u32x4 pk;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    acc[i][2 * e] = __builtin_fmaf(wj, __uint_as_float(v[e] << 16), acc[i][2 * e]);
-                    acc[i][2 * e + 1] = __builtin_fmaf(wj, __uint_as_float(v[e] & 0xffff0000u), acc[i][2 * e + 1]);
+                    part = __builtin_fmaf(g[i][2 * e], __uint_as_float(v[e] << 16), part);
+                    part = __builtin_fmaf(g[i][2 * e + 1], __uint_as_float(v[e] & 0xffff0000u), part);
+                    pk[e] = bf16_rne(__fmul_rn(wj, g[i][2 * e])) | (bf16_rne(__fmul_rn(wj, g[i][2 * e + 1])) << 16);
                 }
+                store_row16<MS_COMBINE_NT_STORE>(pk, gy + i * kWave + lane);
             }
         }
-    }
-    u32x4* o = out + (int64_t)t * V + c0;
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-        if (FULL || c0 + i * kWave + lane < V) {
-            u32x4 pk;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pk[e] = bf16_rne(acc[i][2 * e]) | (bf16_rne(acc[i][2 * e + 1]) << 16);
-            store_row16<MS_COMBINE_NT_STORE>(pk, o + i * kWave + lane);
-        }
+        for (int m = kWave / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
+        if (lane == j) mine = part;
     }
+    if (lane < k) dots[((int64_t)t * rs.cpr + chunk) * k + lane] = mine;
+}
+
+// grad_w[t][j] = sum over chunks c (ascending) of dots[t][c][j].
+__global__ __launch_bounds__(kBlock) void gate_grad_kernel(const float* __restrict__ dots, int T, int k, int cpr,
+                                                           float* __restrict__ grad_w,
+                                                           const int32_t* __restrict__ status)
+{
+    if (status[0] != MOE_SHUFFLE_OK) return;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= (int64_t)T * k) return;
+    const int64_t t = i / k, j = i - t * k;
+    const float* d = dots + t * cpr * k + j;
+    float acc = 0.0f;
+    for (int c = 0; c < cpr; ++c) acc += d[(int64_t)c * k];
+    grad_w[i] = acc;
 }
 
 template <int U>
-static hipError_t launch_combine_u(const void* ye, const float* w, const int32_t* rows, void* out, int T, int k, int V,
-                                   const int32_t* status, hipStream_t s)
+static hipError_t launch_combine_bwd_u(const void* grad_out, const void* ye, const float* w, const int32_t* comb_row,
+                                       void* grad_ye, float* grad_w, float* dots, int T, int k, int V,
+                                       const int32_t* status, hipStream_t s)
 {
     RowSplit rs;
     if (!make_split(V, U, T, &rs)) return hipErrorInvalidValue;
     const int64_t units = (int64_t)T * rs.cpr;
     const dim3 grid((unsigned)((units + kWavesPerBlock - 1) / kWavesPerBlock));
     const size_t lds = tile_lds_bytes(k, 2);
+    const u32x4* gp = (const u32x4*)grad_out;
     const u32x4* yp = (const u32x4*)ye;
-    u32x4* op = (u32x4*)out;
+    u32x4* gyp = (u32x4*)grad_ye;
     if (V % (kWave * U) == 0)
-        hipLaunchKernelGGL((combine_rows_kernel<U, true>), grid, dim3(kBlock), lds, s, yp, w, rows, op, T, k, rs,
-                           status);
+        hipLaunchKernelGGL((combine_bwd_kernel<U, true>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp, dots,
+                           T, k, rs, status);
     else
-        hipLaunchKernelGGL((combine_rows_kernel<U, false>), grid, dim3(kBlock), lds, s, yp, w, rows, op, T, k, rs,
-                           status);
+        hipLaunchKernelGGL((combine_bwd_kernel<U, false>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
+                           dots, T, k, rs, status);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)T * k;
+    hipLaunchKernelGGL(gate_grad_kernel, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, dots, T, k,
+                       rs.cpr, grad_w, status);
     return hipGetLastError();
 }
 
-// Combine gathers from the whole expert-major buffer; past a few GiB of it,
-// whole-row units (8 KiB) measured faster than 1 KiB units on the MI355X
-// (65536 tokens x 8 x 8 KiB: 0.80 ms against 0.94 ms), below it 1 KiB units
-// were as fast or faster.
-#ifndef MS_COMBINE_UNIT_LARGE
-#define MS_COMBINE_UNIT_LARGE 8
-#endif
-#ifndef MS_COMBINE_LARGE_BYTES
-#define MS_COMBINE_LARGE_BYTES (2ll << 30)
-#endif
-
-hipError_t launch_combine_rows(const void* ye, const float* w, const int32_t* rows, void* out, int T, int k, int H,
-                               const int32_t* status, hipStream_t s)
+hipError_t launch_combine_backward(const void* grad_out, const void* ye, const float* w, const int32_t* comb_row,
+                                   void* grad_ye, float* grad_w, float* dots, int T, int k, int H,
+                                   const int32_t* status, hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
-    const int V = H / 8;
-    const bool large = (int64_t)T * k * H * 2 > (int64_t)MS_COMBINE_LARGE_BYTES;
-    switch (fit_unit(V, large ? MS_COMBINE_UNIT_LARGE : MS_COMBINE_UNIT)) {
-        case 1: return launch_combine_u<1>(ye, w, rows, out, T, k, V, status, s);
-        case 2: return launch_combine_u<2>(ye, w, rows, out, T, k, V, status, s);
-        case 4: return launch_combine_u<4>(ye, w, rows, out, T, k, V, status, s);
-        default: return launch_combine_u<8>(ye, w, rows, out, T, k, V, status, s);
-    }
+    return launch_combine_bwd_u<1>(grad_out, ye, w, comb_row, grad_ye, grad_w, dots, T, k, H / 8, status, s);
 }
 
 }  // namespace ms

@@ -100,3 +100,62 @@ def check_case(idx, x, w, H, E, R, ye=None, name=""):
         drt = pins.bf16_ulp_distance(g["out_rt"], ort)
         assert (int(drt.max()) if drt.size else 0) <= 1
     return g, o
+
+
+def abs_dot(comb_row, g_bits, ye_bits, chunk=256):
+    """sum_h |grad_out[t,h] * ye[q,h]| for every (t, j), in float64, chunked."""
+    T, k = comb_row.shape
+    out = np.zeros((T, k))
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        g = np.abs((g_bits[t0:t1].astype(np.uint32) << np.uint32(16)).view(np.float32)).astype(np.float64)
+        for j in range(k):
+            y = np.abs((ye_bits[comb_row[t0:t1, j]].astype(np.uint32) << np.uint32(16)).view(np.float32))
+            out[t0:t1, j] = (g * y).sum(axis=1)
+    return out
+
+
+def check_backward_case(idx, w, H, E, R, ye, grad_xe, grad_out, name=""):
+    """Dispatch backward, rank-partial combine and combine backward on the GPU
+    against the oracle: bf16 rows bit-exact; the fp32 gate gradient within
+    its summation bound of the oracle's fp64 value."""
+    T, k = idx.shape
+    KR = min(k, R)
+    orc = oracle.get()
+    say(f"[bwd] {name} T={T} H={H} E={E} k={k} R={R}")
+    dims = ms.dims_of(T, H, E, k, R)
+    ws = torch.empty(ms.moe_shuffle_workspace_size(dims), dtype=torch.uint8, device="cuda")
+    plan = ms.moe_shuffle_plan(dims, torch.from_numpy(np.ascontiguousarray(idx)).cuda(), ws)
+    rows = max(T * KR, 1)
+    dev = lambda a, n: to_dev16(a) if n else torch.empty((1, H), dtype=torch.int16, device="cuda")  # noqa: E731
+    gxe_d, ye_d, gout_d = dev(grad_xe, T), dev(ye, T), dev(grad_out, T)
+    w_d = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).cuda() if T else \
+        torch.empty(1, dtype=torch.float32, device="cuda")
+    full = lambda r: torch.full((max(r, 1), H), SENTINEL, dtype=torch.int16, device="cuda")  # noqa: E731
+    gxr, gx, part, out, gye = full(rows), full(T), full(rows), full(T), full(T * k)
+    gw = torch.full((max(T * k, 1),), float("nan"), dtype=torch.float32, device="cuda")
+    ms.moe_shuffle_dispatch_backward(plan, gxe_d, gxr, gx)
+    ms.moe_shuffle_combine_rank_partial(plan, ye_d, w_d, part, out)
+    ms.moe_shuffle_combine_backward(plan, gout_d, ye_d, w_d, gye, gw)
+    info = ms.moe_shuffle_plan_query(plan)
+    torch.cuda.synchronize()
+    N = info["N"]
+    rc, o = orc.plan(idx, H, E, R)
+    assert rc == 0 and o["N"] == N
+    o_gxr, o_gx = orc.dispatch_backward(o, grad_xe, T, E, k, R)
+    np.testing.assert_array_equal(to_host16(gxr)[:N], o_gxr, err_msg="grad_xr")
+    assert np.all(to_host16(gxr)[N:] == SENTINEL)
+    np.testing.assert_array_equal(to_host16(gx)[:T], o_gx, err_msg="grad_x")
+    o_part, o_out = orc.combine_rank_partial(o, ye, w, E, R)
+    np.testing.assert_array_equal(to_host16(part)[:N], o_part, err_msg="partial")
+    np.testing.assert_array_equal(to_host16(out)[:T], o_out, err_msg="rank-partial out")
+    o_gye, o_gw = orc.combine_backward(o["comb_row"], grad_out, ye, w, E, R)
+    np.testing.assert_array_equal(to_host16(gye)[:T * k], o_gye, err_msg="grad_ye")
+    if T:
+        got = gw.cpu().numpy()[:T * k].reshape(T, k).astype(np.float64)
+        cpr = -(-(H // 8) // 64)
+        bound = (8 + 6 + cpr + 2) * 2.0 ** -24 * abs_dot(o["comb_row"], grad_out, ye) + 2.0 ** -126
+        err = np.abs(got - o_gw)
+        say(f"[bwd] {name} N={N} grad_w max err / bound {float((err / bound).max()):.3g}")
+        assert np.all(err <= bound)
+    ms.moe_shuffle_plan_destroy(plan)

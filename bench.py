@@ -104,6 +104,20 @@ def pmc_summary(args):
             vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
         return vals
 
+    if not args.fetch_csv:  # kernel trace only (no counter runs)
+        stats = {r["Name"]: r for r in csv.DictReader(open(args.trace_stats))}
+        lines = [f"# Kernel time — {cfg.name}, path {args.path}", "",
+                 f"T={T} H={H} E={E} k={k} R={R}, N={N}; kernel source sha256[:16] {args.src_sha or source_digest()}.",
+                 "", "Command (run from the repository root on one MI355X):", ""]
+        lines += [f"    {c}" for c in args.commands] + ["", "| kernel | calls | avg us | min us | max us |",
+                                                          "|---|---|---|---|---|"]
+        for n, r in stats.items():
+            lines.append(f"| `{n.split('(')[0]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                         f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+        with open(os.path.join(args.out_dir, f"kernels_{args.path}_{cfg.name}.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
     fetch, write = per_kernel(args.fetch_csv), per_kernel(args.write_csv)
     copy_name = next(n for n in fetch if "copyBuffer" in n)
     f_factor = copy_bytes / (max(fetch[copy_name]) * 1024)
@@ -111,7 +125,7 @@ def pmc_summary(args):
     stats = {r["Name"]: r for r in csv.DictReader(open(args.trace_stats))}
 
     short = {"dispatch_send_kernel": "send", "dispatch_fanout_kernel": "fanout", "combine_rows_kernel": "combine"}
-    digest = source_digest()
+    digest = args.src_sha or source_digest()
     rows = []
     for name in sorted(set(fetch) & set(write)):
         if "copyBuffer" in name:
@@ -199,11 +213,20 @@ def bench_path(args):
     if args.path == "backward":
         gxe_h = synth.wide_bf16(rng, (T * k, H), -8, 8)
         gout_h = synth.wide_bf16(rng, (T, H), -8, 8)
-        gxe, gout = g16(gxe_h), g16(gout_h)
+        gxe = g16(gxe_h)
+        # rotate copies of the token-major input, as the forward path does with x
+        nb = int(min(8, max(2, -(-(512 << 20) // max(T * H * 2, 1)))))
+        gouts = [g16(gout_h)]
+        gouts += [gouts[0].clone() for _ in range(nb - 1)]
+        turn = [0]
+
+        def next_gout():
+            turn[0] += 1
+            return gouts[turn[0] % nb]
         gye = torch.empty((T * k, H), dtype=torch.int16, device=dev)
         gw = torch.empty((T * k,), dtype=torch.float32, device=dev)
         names = ("combine_bwd", "sum_expert_rows", "sum_rank_rows")
-        calls = (lambda: ms.moe_shuffle_combine_backward(plan, gout, ye, w, gye, gw),
+        calls = (lambda: ms.moe_shuffle_combine_backward(plan, next_gout(), ye, w, gye, gw),
                  lambda: ms.moe_shuffle_sum_expert_rows(plan, gxe, None, rows),
                  lambda: ms.moe_shuffle_sum_rank_rows(plan, rows, out))
     else:
@@ -263,6 +286,95 @@ def bench_path(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_pipelined(args):
+    """--path pipelined: the forward step with dispatch and combine run per
+    chunk of tokens, chunk i's combine on a second stream overlapping chunk
+    i+1's dispatch.  Reports its time next to the sequential step's."""
+    import numpy as np
+    import torch
+
+    import moe_expert_token_amd as ms
+    import synth
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.config]
+    T, H, E, k, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.R
+    KR = min(k, R)
+    inp = synth.make_inputs(cfg, args.seed)
+    nb = int(min(8, max(2, -(-(512 << 20) // max(T * H * 2, 1)))))
+    x0 = torch.from_numpy(inp["x"].view(np.int16)).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(nb - 1)]
+    idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    w = torch.from_numpy(inp["topk_w"]).to(dev)
+    dims = ms.dims_of(T, H, E, k, R)
+    ws = torch.empty(ms.moe_shuffle_workspace_size(dims), dtype=torch.uint8, device=dev)
+    xr = torch.empty((T * KR, H), dtype=torch.int16, device=dev)
+    xe = torch.empty((T * k, H), dtype=torch.int16, device=dev)
+    out = torch.empty((T, H), dtype=torch.int16, device=dev)
+    tile = 256
+    bounds = sorted({min(T, -(-(i * T // args.chunks) // tile) * tile) for i in range(args.chunks)} | {T})
+    bounds = [0] + [b for b in bounds if b > 0]
+    a = torch.cuda.current_stream()
+    bstream = torch.cuda.Stream()
+
+    def step_seq(i):
+        p = ms.moe_shuffle_plan(dims, idx, ws)
+        ms.moe_shuffle_dispatch(p, xs[i % nb], xr, xe)
+        ms.moe_shuffle_combine(p, xe, w, out)
+        return p
+
+    def step_pipe(i):
+        p = ms.moe_shuffle_plan(dims, idx, ws)
+        x = xs[i % nb]
+        for t0, t1 in zip(bounds[:-1], bounds[1:]):
+            ms.moe_shuffle_dispatch_range(p, x, xr, xe, t0, t1, stream=a)
+            ev = torch.cuda.Event()
+            ev.record(a)
+            bstream.wait_event(ev)
+            ms.moe_shuffle_combine_range(p, xe, w, out, t0, t1, stream=bstream)
+        a.wait_stream(bstream)
+        return p
+
+    def timed(fn):
+        for i in range(args.warmup):
+            ms.moe_shuffle_plan_destroy(fn(i))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        plans = [fn(i) for i in range(args.steps)]
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) * 1e3 / args.steps
+        for p in plans[:-1]:
+            ms.moe_shuffle_plan_destroy(p)
+        return dt, plans[-1]
+
+    seq_ms, p = timed(step_seq)
+    ms.moe_shuffle_plan_destroy(p)
+    pipe_ms, p = timed(step_pipe)
+    N = ms.moe_shuffle_plan_query(p)["N"]
+    B = algorithmic_bytes(T, H, k, N)
+    parity = None
+    if not args.no_parity:
+        import oracle
+        orc = oracle.get()
+        rc, o = orc.plan(inp["topk_idx"], H, E, R)
+        oxr, oxe = orc.dispatch(o, inp["x"], E, k, R)
+        oout = orc.combine(o["comb_row"], oxe, inp["topk_w"], E, R)
+        parity = {"xr_bitexact": bool(np.array_equal(xr[:N].cpu().numpy().view(np.uint16), oxr)),
+                  "xe_bitexact": bool(np.array_equal(xe.cpu().numpy().view(np.uint16), oxe)),
+                  "out_bitexact": bool(np.array_equal(out.cpu().numpy().view(np.uint16), oout))}
+    ms.moe_shuffle_plan_destroy(p)
+    value = B["total"] / (pipe_ms * 1e-3) / 1e9
+    rec = {"metric": "pipelined forward shuffle effective HBM GB/s (fraction of peak), 1 GPU",
+           "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(pipe_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": cfg.name, "T": T, "H": H, "E": E, "k": k, "R": R, "N": N, "path": "pipelined",
+                      "token_chunks": bounds},
+           "frac_of_peak": round(value / PEAK_HBM_GBPS, 4), "sequential_ms_per_step": round(seq_ms, 4),
+           "speedup_vs_sequential": round(seq_ms / pipe_ms, 4), "algorithmic_bytes": B, "parity": parity,
+           "roofline": None, "cpu_baseline": None, "kernel_src_sha256_16": source_digest()}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,7 +385,8 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=12.0, help="CPU-oracle timing budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
-    ap.add_argument("--path", default="forward", choices=("forward", "backward", "rank-partial"),
+    ap.add_argument("--chunks", type=int, default=4, help="token chunks for --path pipelined")
+    ap.add_argument("--path", default="forward", choices=("forward", "backward", "rank-partial", "pipelined"),
                     help="forward (default): plan + dispatch + combine; backward: combine and dispatch backward; "
                          "rank-partial: combine through one row per (token, rank)")
     ap.add_argument("--pmc-summary", action="store_true", help="summarise rocprofv3 CSVs into profiles/ (no GPU)")
@@ -282,6 +395,7 @@ def main():
     ap.add_argument("--trace-stats")
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--commands", nargs="*", default=[])
+    ap.add_argument("--src-sha", default=None, help="kernel source hash of the profiled run (default: current)")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args)
@@ -307,6 +421,9 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda:0")
+    if args.path == "pipelined":
+        bench_pipelined(args)
+        return
     if args.path != "forward":
         bench_path(args)
         return

@@ -173,6 +173,25 @@ int moe_shuffle_combine(moe_shuffle_plan_t plan, const void* ye, const float* to
                         void* stream);
 
 /*
+ * Token ranges (DySHARP write-up, section 6 / Fig. 12: the shuffle runs per
+ * group of tokens, so the dispatch of one group overlaps later stages of the
+ * previous one).  Both calls act on the tokens [t0, t1) of the plan: t0 a
+ * multiple of 256 (the plan's token tile), t1 a multiple of 256 or T.
+ * Rows land exactly where the whole-batch calls put them: the rank rows of
+ * the range are a contiguous sub-range of every rank segment, its expert
+ * rows a contiguous sub-range of every expert segment.  Buffers are the
+ * whole-batch ones (x [T,H], xr, xe [T*k,H], ye, topk_w [T,k], out [T,H]);
+ * calls on disjoint ranges may run concurrently on different streams, and
+ * combine of a range may start once that range's dispatch (and expert work)
+ * is complete.  Errors as for moe_shuffle_dispatch / moe_shuffle_combine,
+ * plus MOE_SHUFFLE_E_INVALID_ARG for a range off those boundaries.
+ */
+int moe_shuffle_dispatch_range(moe_shuffle_plan_t plan, const void* x, void* xr, int64_t xr_rows, void* xe,
+                               int32_t t0, int32_t t1, void* stream);
+int moe_shuffle_combine_range(moe_shuffle_plan_t plan, const void* ye, const float* topk_w, void* out, int32_t t0,
+                              int32_t t1, void* stream);
+
+/*
  * The return path with one row per (token, rank) pair, and the training
  * direction.  The FUSCO abstract reports training latency, so the shuffle
  * also runs backwards; the DySHARP write-up (section 2 / Fig. 1) notes that

@@ -25,6 +25,7 @@ EXPORTS = (
     "moe_shuffle_plan_arrays_get", "moe_shuffle_plan_destroy", "moe_shuffle_strerror",
     "moe_shuffle_last_hip_error", "moe_shuffle_sum_expert_rows", "moe_shuffle_sum_rank_rows",
     "moe_shuffle_dispatch_backward", "moe_shuffle_combine_rank_partial", "moe_shuffle_combine_backward",
+    "moe_shuffle_dispatch_range", "moe_shuffle_combine_range",
 )
 
 
@@ -86,6 +87,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_shuffle_dispatch_backward": (ctypes.c_int, [_vp, _vp, _vp, i64, _vp, _vp]),
         "moe_shuffle_combine_rank_partial": (ctypes.c_int, [_vp, _vp, _vp, _vp, i64, _vp, _vp]),
         "moe_shuffle_combine_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+        "moe_shuffle_dispatch_range": (ctypes.c_int, [_vp, _vp, _vp, i64, _vp, ctypes.c_int32, ctypes.c_int32, _vp]),
+        "moe_shuffle_combine_range": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -207,6 +210,16 @@ def moe_shuffle_combine_rank_partial(plan: Plan, ye, topk_w, partial, out, strea
 def moe_shuffle_combine_backward(plan: Plan, grad_out, ye, topk_w, grad_ye, grad_w, stream=None):
     _check("moe_shuffle_combine_backward", load().moe_shuffle_combine_backward(
         plan.handle, _ptr(grad_out), _ptr(ye), _ptr(topk_w), _ptr(grad_ye), _ptr(grad_w), _stream(stream)))
+
+
+def moe_shuffle_dispatch_range(plan: Plan, x, xr, xe, t0: int, t1: int, stream=None):
+    _check("moe_shuffle_dispatch_range", load().moe_shuffle_dispatch_range(
+        plan.handle, _ptr(x), _ptr(xr), xr.shape[0], _ptr(xe), int(t0), int(t1), _stream(stream)))
+
+
+def moe_shuffle_combine_range(plan: Plan, ye, topk_w, out, t0: int, t1: int, stream=None):
+    _check("moe_shuffle_combine_range", load().moe_shuffle_combine_range(
+        plan.handle, _ptr(ye), _ptr(topk_w), _ptr(out), int(t0), int(t1), _stream(stream)))
 
 
 def moe_shuffle_plan_query(plan: Plan, stream=None) -> dict:

@@ -358,6 +358,52 @@ int moe_shuffle_combine_backward(moe_shuffle_plan_t plan, const void* grad_out, 
     return e == hipSuccess ? MOE_SHUFFLE_OK : hip_fail(e);
 }
 
+int moe_shuffle_dispatch_range(moe_shuffle_plan_t plan, const void* x, void* xr, int64_t xr_rows, void* xe,
+                               int32_t t0, int32_t t1, void* stream)
+{
+    int rc = check_plan(plan);
+    if (rc) return rc;
+    const ms::Layout& L = plan->L;
+    if (t0 < 0 || t1 < t0 || t1 > L.T || t0 % ms::kPlanTile != 0 || (t1 % ms::kPlanTile != 0 && t1 != L.T))
+        return MOE_SHUFFLE_E_INVALID_ARG;
+    if (t1 == t0) return MOE_SHUFFLE_OK;
+    rc = check_send(plan, x, xr, xr_rows);
+    if (rc) return rc;
+    rc = check_fanout(plan, xr, xr_rows, xe);
+    if (rc) return rc;
+    const size_t row = (size_t)L.H * 2;
+    if (overlap(x, row * L.T, xe, row * (size_t)L.T * L.k)) return MOE_SHUFFLE_E_INVALID_ARG;
+    const int32_t* status = at<int32_t>(plan, L.status);
+    hipError_t e = ms::launch_fanout_rows(true, (const char*)x + row * (size_t)t0, xr,
+                                          at<int32_t>(plan, L.tok_rank_row) + (size_t)t0 * L.KR, L.KR, t1 - t0,
+                                          nullptr, L.H, status, (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = ms::launch_fanout_range(xr, xe, at<int32_t>(plan, L.fan_dst), L.D, at<int32_t>(plan, L.rank_offset),
+                                    at<int32_t>(plan, L.tile_base), at<int32_t>(plan, L.col_total), L.E, L.R, L.ntiles,
+                                    t0, t1, L.T, L.KR, L.H, status, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_SHUFFLE_OK : hip_fail(e);
+}
+
+int moe_shuffle_combine_range(moe_shuffle_plan_t plan, const void* ye, const float* topk_w, void* out, int32_t t0,
+                              int32_t t1, void* stream)
+{
+    int rc = check_plan(plan);
+    if (rc) return rc;
+    const ms::Layout& L = plan->L;
+    if (t0 < 0 || t1 < t0 || t1 > L.T || t0 % ms::kPlanTile != 0 || (t1 % ms::kPlanTile != 0 && t1 != L.T))
+        return MOE_SHUFFLE_E_INVALID_ARG;
+    if (t1 == t0) return MOE_SHUFFLE_OK;
+    if (!ye || !topk_w || !out) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (misaligned(ye, 16) || misaligned(out, 16) || misaligned(topk_w, 4)) return MOE_SHUFFLE_E_ALIGN;
+    const size_t row = (size_t)L.H * 2;
+    if (overlap(ye, row * (size_t)L.T * L.k, out, row * L.T)) return MOE_SHUFFLE_E_INVALID_ARG;
+    const hipError_t e = ms::launch_combine_rows(ye, topk_w + (size_t)t0 * L.k,
+                                                 at<int32_t>(plan, L.comb_row) + (size_t)t0 * L.k,
+                                                 (char*)out + row * (size_t)t0, t1 - t0, L.k, L.H,
+                                                 at<int32_t>(plan, L.status), (hipStream_t)stream);
+    return e == hipSuccess ? MOE_SHUFFLE_OK : hip_fail(e);
+}
+
 int moe_shuffle_plan_query(moe_shuffle_plan_t plan, void* stream, moe_shuffle_plan_info* info)
 {
     int rc = check_plan(plan);

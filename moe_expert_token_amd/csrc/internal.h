@@ -68,6 +68,12 @@ hipError_t launch_sum_expert_rows(const void* src, int64_t src_rows, const float
 hipError_t launch_sum_rank_rows(const void* src, int64_t src_rows, const int32_t* tok_rank_row, int KR, void* out,
                                 int T, int H, const int32_t* status, hipStream_t s);
 
+// The fan-out of the rank rows that belong to tokens [t0, t1) (t0, t1
+// multiples of kPlanTile, or t1 = T).
+hipError_t launch_fanout_range(const void* xr, void* xe, const int32_t* fan_dst, int D, const int32_t* rank_offset,
+                               const int32_t* tile_base, const int32_t* col_total, int E, int R, int ntiles, int t0,
+                               int t1, int T, int KR, int H, const int32_t* status, hipStream_t s);
+
 // grad_ye[q(t,j)] = bf16(w[t][j] * grad_out[t]); grad_w[t][j] = <grad_out[t], ye[q(t,j)]>.
 hipError_t launch_combine_backward(const void* grad_out, const void* ye, const float* w, const int32_t* comb_row,
                                    void* grad_ye, float* grad_w, float* dots, int T, int k, int H,

@@ -89,25 +89,10 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* s_wsum, int* tot
     return v + before;
 }
 
-// Exclusive scan of src[0..n) into dst[0..n] (dst[n] = sum), block-wide.
-__device__ void block_exclusive_scan_array(const int32_t* src, int n, int* dst, int* s_wsum)
-{
-    int carry = 0;
-    for (int base = 0; base < n; base += kBlock) {
-        const int i = base + (int)threadIdx.x;
-        const int v = i < n ? src[i] : 0;
-        int total;
-        const int incl = block_inclusive_scan(v, s_wsum, &total);
-        if (i < n) dst[i] = carry + incl - v;
-        carry += total;
-    }
-    if (threadIdx.x == 0) dst[n] = carry;
-    __syncthreads();
-}
-
 // ---------------------------------------------------------------- plan_count
 
 // hist is column-major [(C+1)][ntiles]; column C holds the tile's error flag.
+template <int KMAX>
 __global__ __launch_bounds__(kBlock) void plan_count_kernel(const int32_t* __restrict__ idx, int T, int k,
                                                             int E, FastDiv epr, int C, int ntiles,
                                                             int32_t* __restrict__ hist)
@@ -116,22 +101,38 @@ __global__ __launch_bounds__(kBlock) void plan_count_kernel(const int32_t* __res
     __shared__ int s_slots, s_ecount;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int tile = blockIdx.x;
+    const int t = tile * kPlanTile + tid;
+
+    // The ids first (their load overlaps the clearing of the masks).
+    int ev[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) ev[j] = -1;
+    if (t < T) {
+        const int32_t* row = idx + (int64_t)t * k;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (j < k) ev[j] = row[j];
+    }
     if (tid == 0) { s_slots = 0; s_ecount = 0; }
     for (int i = tid; i < kWavesPerBlock * C; i += kBlock) s_mask[i] = 0ull;
     __syncthreads();
 
-    const int t = tile * kPlanTile + tid;
     int bad = 0, nslots = 0;
     if (t < T) {
-        const int32_t* row = idx + (int64_t)t * k;
         const unsigned long long bit = 1ull << lane;
         unsigned long long* m = s_mask + wave * C;
-        for (int j = 0; j < k; ++j) {
-            const int e = row[j];
-            if ((unsigned)e >= (unsigned)E) { bad = 1; continue; }
-            ++nslots;
-            atomicOr(&m[e], bit);
-            atomicOr(&m[E + fdiv(e, epr)], bit);
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            if (j < k) {
+                const int e = ev[j];
+                if ((unsigned)e >= (unsigned)E) {
+                    bad = 1;
+                } else {
+                    ++nslots;
+                    atomicOr(&m[e], bit);
+                    atomicOr(&m[E + fdiv(e, epr)], bit);
+                }
+            }
         }
     }
     if (nslots) atomicAdd(&s_slots, nslots);
@@ -201,46 +202,23 @@ struct PlaceArgs {
 template <int KMAX>
 __global__ __launch_bounds__(kBlock) void plan_place_kernel(PlaceArgs a)
 {
-    if (a.status[0] != MOE_SHUFFLE_OK) return;
     extern __shared__ unsigned long long s_dyn[];
     const int C = a.C, E = a.E, R = a.R;
     unsigned long long* s_mask = s_dyn;                        // [4][C]
     int* s_wbase = (int*)(s_mask + kWavesPerBlock * C);        // [4][C]
-    int* s_off = s_wbase + kWavesPerBlock * C;                 // [E+1] then [R+1]
     __shared__ int s_wsum[kWavesPerBlock];
+    __shared__ int s_etotal;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int tile = blockIdx.x;
-
-    // Segment offsets from the column totals (every block, redundantly).
-    block_exclusive_scan_array(a.col_total, E, s_off, s_wsum);
-    block_exclusive_scan_array(a.col_total + E, R, s_off + E + 1, s_wsum);
-
-    if (tile == 0) {
-        for (int e = tid; e < E; e += kBlock) {
-            const int cnt = a.col_total[e];
-            a.expert_count[e] = cnt;
-            a.expert_offset[e] = s_off[e];
-            int32_t* seg = a.expert_segs + 4 * e;
-            seg[0] = e / a.Epr; seg[1] = e; seg[2] = s_off[e]; seg[3] = cnt;
-        }
-        for (int r = tid; r < R; r += kBlock) {
-            const int cnt = a.col_total[E + r];
-            a.rank_count[r] = cnt;
-            a.rank_offset[r] = s_off[E + 1 + r];
-            int32_t* seg = a.rank_segs + 4 * r;
-            seg[0] = r; seg[1] = -1; seg[2] = s_off[E + 1 + r]; seg[3] = cnt;
-        }
-        if (tid == 0) {
-            a.expert_offset[E] = s_off[E];
-            a.rank_offset[R] = s_off[E + 1 + R];
-            a.n_rank_rows[0] = s_off[E + 1 + R];
-        }
-    }
-
-    // This thread's token: its top-k ids in registers (unused slots sort last).
     const int t = tile * kPlanTile + tid;
     const int k = a.k;
+    constexpr int kCols = kMaxCols / kBlock;  // histogram columns per thread
+
+    // Every global load first, so their latencies overlap: the status word,
+    // this thread's top-k ids, and for each column it owns the column total
+    // and this tile's base within the column.
+    const int status = a.status[0];
     int ev[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) ev[j] = 0x7fffffff;
@@ -250,10 +228,19 @@ __global__ __launch_bounds__(kBlock) void plan_place_kernel(PlaceArgs a)
         for (int j = 0; j < KMAX; ++j)
             if (j < k) ev[j] = row[j];
     }
+    int ct[kCols], tb[kCols];
+#pragma unroll
+    for (int i = 0; i < kCols; ++i) {
+        const int c = tid + i * kBlock;
+        ct[i] = c < C ? a.col_total[c] : 0;
+        tb[i] = c < C ? a.tile_base[(int64_t)c * a.ntiles + tile] : 0;
+    }
 
-    // Rebuild this tile's masks.
     for (int i = tid; i < kWavesPerBlock * C; i += kBlock) s_mask[i] = 0ull;
     __syncthreads();
+    if (status != MOE_SHUFFLE_OK) return;
+
+    // This tile's masks.
     if (t < a.T) {
         const unsigned long long bit = 1ull << lane;
         unsigned long long* m = s_mask + wave * C;
@@ -264,16 +251,57 @@ __global__ __launch_bounds__(kBlock) void plan_place_kernel(PlaceArgs a)
                 atomicOr(&m[E + fdiv(ev[j], a.epr)], bit);
             }
     }
-    __syncthreads();
 
-    // First row of every column for each wave of this tile.
-    for (int c = tid; c < C; c += kBlock) {
-        int run = (c < E ? s_off[c] : s_off[E + 1 + (c - E)]) + a.tile_base[(int64_t)c * a.ntiles + tile];
+    // One exclusive scan over all columns, experts first then ranks; a rank
+    // column's segment offset is its prefix minus the expert total.
+    int excl[kCols];
+    int carry = 0;
+#pragma unroll
+    for (int i = 0; i < kCols; ++i) {
+        if (i * kBlock >= C) break;  // uniform
+        int total;
+        const int incl = block_inclusive_scan(ct[i], s_wsum, &total);
+        excl[i] = carry + incl - ct[i];
+        carry += total;
+    }
+#pragma unroll
+    for (int i = 0; i < kCols; ++i)
+        if (tid + i * kBlock == E) s_etotal = excl[i];
+    __syncthreads();
+    const int etot = s_etotal;
+
+    // Segment offsets (tile 0 publishes them) and the first row of every
+    // column for each wave of this tile.
+#pragma unroll
+    for (int i = 0; i < kCols; ++i) {
+        const int c = tid + i * kBlock;
+        if (c >= C) break;
+        const int off = c < E ? excl[i] : excl[i] - etot;
+        if (tile == 0) {
+            if (c < E) {
+                a.expert_count[c] = ct[i];
+                a.expert_offset[c] = off;
+                int32_t* seg = a.expert_segs + 4 * c;
+                seg[0] = fdiv(c, a.epr); seg[1] = c; seg[2] = off; seg[3] = ct[i];
+            } else {
+                const int r = c - E;
+                a.rank_count[r] = ct[i];
+                a.rank_offset[r] = off;
+                int32_t* seg = a.rank_segs + 4 * r;
+                seg[0] = r; seg[1] = -1; seg[2] = off; seg[3] = ct[i];
+            }
+        }
+        int run = off + tb[i];
 #pragma unroll
         for (int w = 0; w < kWavesPerBlock; ++w) {
             s_wbase[w * C + c] = run;
             run += __popcll(s_mask[w * C + c]);
         }
+    }
+    if (tile == 0 && tid == 0) {
+        a.expert_offset[E] = etot;
+        a.rank_offset[R] = carry - etot;
+        a.n_rank_rows[0] = carry - etot;
     }
     __syncthreads();
     if (t >= a.T) return;
@@ -335,8 +363,18 @@ hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)
     const int ntiles = L.ntiles;
     const size_t lds_count = sizeof(unsigned long long) * kWavesPerBlock * L.C;
     const FastDiv epr = make_fastdiv(L.Epr);
-    hipLaunchKernelGGL(plan_count_kernel, dim3(ntiles), dim3(kBlock), lds_count, s, P.idx, L.T, L.k, L.E,
-                       epr, L.C, ntiles, P.tile_hist);
+    if (L.k <= 8)
+        hipLaunchKernelGGL(plan_count_kernel<8>, dim3(ntiles), dim3(kBlock), lds_count, s, P.idx, L.T, L.k, L.E,
+                           epr, L.C, ntiles, P.tile_hist);
+    else if (L.k <= 16)
+        hipLaunchKernelGGL(plan_count_kernel<16>, dim3(ntiles), dim3(kBlock), lds_count, s, P.idx, L.T, L.k, L.E,
+                           epr, L.C, ntiles, P.tile_hist);
+    else if (L.k <= 32)
+        hipLaunchKernelGGL(plan_count_kernel<32>, dim3(ntiles), dim3(kBlock), lds_count, s, P.idx, L.T, L.k, L.E,
+                           epr, L.C, ntiles, P.tile_hist);
+    else
+        hipLaunchKernelGGL(plan_count_kernel<64>, dim3(ntiles), dim3(kBlock), lds_count, s, P.idx, L.T, L.k, L.E,
+                           epr, L.C, ntiles, P.tile_hist);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(plan_scan_kernel, dim3(L.C + 1), dim3(kBlock), 0, s, P.tile_hist, ntiles, L.C,
@@ -354,7 +392,7 @@ hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)
     a.send_token = P.send_token; a.tok_rank_row = P.tok_rank_row; a.fan_src = P.fan_src;
     a.fan_dst = P.fan_dst; a.comb_row = P.comb_row;
     a.rank_segs = P.rank_segs; a.expert_segs = P.expert_segs; a.n_rank_rows = P.n_rank_rows;
-    const size_t lds_place = lds_count + sizeof(int) * (kWavesPerBlock * L.C + L.E + L.R + 2);
+    const size_t lds_place = lds_count + sizeof(int) * kWavesPerBlock * L.C;
     if (L.k <= 8)
         hipLaunchKernelGGL(plan_place_kernel<8>, dim3(ntiles), dim3(kBlock), lds_place, s, a);
     else if (L.k <= 16)
@@ -404,6 +442,24 @@ hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)
 #ifndef MS_COMBINE_NT_STORE
 #define MS_COMBINE_NT_STORE 1
 #endif
+#ifndef MS_SUMX_NT_LOAD
+#define MS_SUMX_NT_LOAD 1
+#endif
+#ifndef MS_SUMX_NT_STORE
+#define MS_SUMX_NT_STORE 1
+#endif
+#ifndef MS_SUMR_NT_LOAD
+#define MS_SUMR_NT_LOAD 1
+#endif
+#ifndef MS_SUMR_NT_STORE
+#define MS_SUMR_NT_STORE 1
+#endif
+#ifndef MS_CBWD_NT_LOAD
+#define MS_CBWD_NT_LOAD 0
+#endif
+#ifndef MS_CBWD_NT_STORE
+#define MS_CBWD_NT_STORE 1
+#endif
 
 template <bool NT>
 __device__ __forceinline__ u32x4 load_row16(const u32x4* p)
@@ -425,20 +481,34 @@ struct RowSplit {
     FastDiv div;  // unit -> row
 };
 
-// Rows of the units of this block: [*first, *first + *count).
-__device__ __forceinline__ void block_rows(int64_t n, const RowSplit& rs, int* first, int* count)
+// First unit of this block.  When the row count is known only on the device
+// the grid is sized by a bound and the blocks past the count have nothing to
+// do; those kernels take the units in reverse block order, so the empty
+// blocks are dispatched first and exit while the real work fills the
+// machine, instead of trailing it (measured on the MI355X, fan-out: skewed
+// workload 537 -> 526 us, long prefill 1383 -> 1328 us; a grid sized by the
+// exact count would be 479 and 1295 us, which needs a host sync).
+template <int WPB>
+__device__ __forceinline__ int block_first_unit(bool reversed)
 {
-    const int u0 = (int)blockIdx.x * kWavesPerBlock;
+    const int b = reversed ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+    return b * WPB;
+}
+
+// Rows touched by units [u0, u0 + WPB): [*first, *first + *count), clipped to n.
+template <int WPB>
+__device__ __forceinline__ void block_rows(int u0, int64_t n, const RowSplit& rs, int* first, int* count)
+{
     const int r0 = fdiv(u0, rs.div);
-    int r1 = fdiv(u0 + kWavesPerBlock - 1, rs.div);
+    int r1 = fdiv(u0 + WPB - 1, rs.div);
     if ((int64_t)r1 >= n) r1 = (int)(n - 1);
     *first = r0;
     *count = r1 - r0 + 1;
 }
 
 // Body shared by the send and fan-out kernels (two names, so that traces and
-// counters tell the two halves of dispatch apart).
-template <int U, bool FULL, bool NTL, bool NTS>
+// counters tell the two halves of dispatch apart).  WPB waves per block.
+template <int U, bool FULL, bool NTL, bool NTS, int WPB>
 __device__ __forceinline__ void fanout_rows(int* s_tile, const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                             const int32_t* __restrict__ map, int width, int64_t n_bound,
                                             const int32_t* __restrict__ n_dev, RowSplit rs,
@@ -446,14 +516,15 @@ __device__ __forceinline__ void fanout_rows(int* s_tile, const u32x4* __restrict
 {
     if (status[0] != MOE_SHUFFLE_OK) return;
     const int64_t n = n_dev ? (int64_t)n_dev[0] : n_bound;
+    const int u0 = block_first_unit<WPB>(n_dev != nullptr);
     int first, count;
-    block_rows(n, rs, &first, &count);
+    block_rows<WPB>(u0, n, rs, &first, &count);
     if (count <= 0) return;  // the whole block is past the last row
-    for (int i = threadIdx.x; i < count * width; i += kBlock) s_tile[i] = map[(int64_t)first * width + i];
+    for (int i = threadIdx.x; i < count * width; i += WPB * kWave) s_tile[i] = map[(int64_t)first * width + i];
     __syncthreads();
 
     const int wave = wave_id(), lane = lane_id();
-    const int u = (int)blockIdx.x * kWavesPerBlock + wave;
+    const int u = u0 + wave;
     const int row = fdiv(u, rs.div);
     if (row >= n) return;
     const int V = rs.V;
@@ -475,14 +546,14 @@ __device__ __forceinline__ void fanout_rows(int* s_tile, const u32x4* __restrict
 }
 
 #define MS_FANOUT_KERNEL(NAME, NTL, NTS)                                                                        \
-    template <int U, bool FULL>                                                                                  \
-    __global__ __launch_bounds__(kBlock) void NAME(const u32x4* __restrict__ src, u32x4* __restrict__ dst,       \
-                                                   const int32_t* __restrict__ map, int width, int64_t n_bound,  \
-                                                   const int32_t* __restrict__ n_dev, RowSplit rs,              \
-                                                   const int32_t* __restrict__ status)                          \
+    template <int U, bool FULL, int WPB>                                                                         \
+    __global__ __launch_bounds__(WPB * kWave) void NAME(const u32x4* __restrict__ src, u32x4* __restrict__ dst,  \
+                                                        const int32_t* __restrict__ map, int width,             \
+                                                        int64_t n_bound, const int32_t* __restrict__ n_dev,     \
+                                                        RowSplit rs, const int32_t* __restrict__ status)        \
     {                                                                                                            \
         extern __shared__ int s_tile[]; /* [rows of this block][width] */                                        \
-        fanout_rows<U, FULL, NTL, NTS>(s_tile, src, dst, map, width, n_bound, n_dev, rs, status);                \
+        fanout_rows<U, FULL, NTL, NTS, WPB>(s_tile, src, dst, map, width, n_bound, n_dev, rs, status);           \
     }
 // x -> xr: source rows are tokens, targets their rank rows.
 MS_FANOUT_KERNEL(dispatch_send_kernel, MS_SEND_NT_LOAD, MS_SEND_NT_STORE)
@@ -507,39 +578,58 @@ static bool make_split(int V, int U, int64_t rows, RowSplit* rs)
     rs->V = V;
     rs->cpr = (V + kWave * U - 1) / (kWave * U);
     rs->div = make_fastdiv(rs->cpr);
-    return rows * rs->cpr + kWavesPerBlock < ((int64_t)1 << 31);
+    return rows * rs->cpr + 64 < ((int64_t)1 << 31);  // units of the last block stay below 2^31
 }
 
-static size_t tile_lds_bytes(int width, int arrays)
+// Kernels whose row count is known only on the device (fan-out, receiver
+// sums) are sized by the host-side bound T*min(k,R); blocks past the true
+// count exit at once (see block_first_unit).  Waves per block for them:
+#ifndef MS_BIG_WAVES
+#define MS_BIG_WAVES 4
+#endif
+constexpr int kWavesBig = MS_BIG_WAVES;
+
+static unsigned grid_for(int64_t units, int wpb) { return (unsigned)((units + wpb - 1) / wpb); }
+
+static size_t tile_lds_bytes(int width, int arrays, int wpb)
 {
-    return sizeof(int) * (size_t)arrays * kWavesPerBlock * width;  // at most one row per wave
+    return sizeof(int) * (size_t)arrays * wpb * width;  // at most one row per wave
+}
+
+template <int U, int WPB>
+static hipError_t launch_fanout_uw(bool send, const void* src, void* dst, const int32_t* map, int width,
+                                   int64_t n_bound, const int32_t* n_dev, int V, const int32_t* status, hipStream_t s)
+{
+    RowSplit rs;
+    if (!make_split(V, U, n_bound, &rs)) return hipErrorInvalidValue;
+    const dim3 grid(grid_for(n_bound * rs.cpr, WPB)), block(WPB * kWave);
+    const size_t lds = tile_lds_bytes(width, 1, WPB);
+    const u32x4* sp = (const u32x4*)src;
+    u32x4* dp = (u32x4*)dst;
+    const bool full = V % (kWave * U) == 0;
+    if (send && full)
+        hipLaunchKernelGGL((dispatch_send_kernel<U, true, WPB>), grid, block, lds, s, sp, dp, map, width, n_bound,
+                           n_dev, rs, status);
+    else if (send)
+        hipLaunchKernelGGL((dispatch_send_kernel<U, false, WPB>), grid, block, lds, s, sp, dp, map, width, n_bound,
+                           n_dev, rs, status);
+    else if (full)
+        hipLaunchKernelGGL((dispatch_fanout_kernel<U, true, WPB>), grid, block, lds, s, sp, dp, map, width, n_bound,
+                           n_dev, rs, status);
+    else
+        hipLaunchKernelGGL((dispatch_fanout_kernel<U, false, WPB>), grid, block, lds, s, sp, dp, map, width,
+                           n_bound, n_dev, rs, status);
+    return hipGetLastError();
 }
 
 template <int U>
 static hipError_t launch_fanout_u(bool send, const void* src, void* dst, const int32_t* map, int width,
                                   int64_t n_bound, const int32_t* n_dev, int V, const int32_t* status, hipStream_t s)
 {
-    RowSplit rs;
-    if (!make_split(V, U, n_bound, &rs)) return hipErrorInvalidValue;
-    const int64_t units = n_bound * rs.cpr;
-    const dim3 grid((unsigned)((units + kWavesPerBlock - 1) / kWavesPerBlock));
-    const size_t lds = tile_lds_bytes(width, 1);
-    const u32x4* sp = (const u32x4*)src;
-    u32x4* dp = (u32x4*)dst;
-    const bool full = V % (kWave * U) == 0;
-    if (send && full)
-        hipLaunchKernelGGL((dispatch_send_kernel<U, true>), grid, dim3(kBlock), lds, s, sp, dp, map, width, n_bound,
-                           n_dev, rs, status);
-    else if (send)
-        hipLaunchKernelGGL((dispatch_send_kernel<U, false>), grid, dim3(kBlock), lds, s, sp, dp, map, width, n_bound,
-                           n_dev, rs, status);
-    else if (full)
-        hipLaunchKernelGGL((dispatch_fanout_kernel<U, true>), grid, dim3(kBlock), lds, s, sp, dp, map, width, n_bound,
-                           n_dev, rs, status);
-    else
-        hipLaunchKernelGGL((dispatch_fanout_kernel<U, false>), grid, dim3(kBlock), lds, s, sp, dp, map, width,
-                           n_bound, n_dev, rs, status);
-    return hipGetLastError();
+    if constexpr (U <= 2) {  // big blocks only with small units (no register pressure)
+        if (n_dev) return launch_fanout_uw<U, kWavesBig>(send, src, dst, map, width, n_bound, n_dev, V, status, s);
+    }
+    return launch_fanout_uw<U, kWavesPerBlock>(send, src, dst, map, width, n_bound, n_dev, V, status, s);
 }
 
 // Largest of {1, 2, 4, 8} not above `want` whose chunk does not exceed the row.
@@ -561,6 +651,120 @@ hipError_t launch_fanout_rows(bool send, const void* src, void* dst, const int32
         case 4: return launch_fanout_u<4>(send, src, dst, map, width, n_bound, n_dev, V, status, s);
         default: return launch_fanout_u<8>(send, src, dst, map, width, n_bound, n_dev, V, status, s);
     }
+}
+
+// ---------------------------------------------------------------- token ranges
+//
+// Dispatch and combine of the tokens [t0, t1) alone, so a caller can
+// pipeline token chunks (DySHARP write-up, section 6 / Fig. 12: dispatch of
+// one group of tokens proceeds while later stages work on the previous one).
+// Rows follow token order inside every segment, so the rank rows of the
+// range are, in each rank segment r, the contiguous rows
+//   [rank_offset[r] + P_r(t0), rank_offset[r] + P_r(t1)),
+// P_r(t) = tokens before t that reach rank r, read from the plan's tile
+// bases (t a multiple of the 256-token plan tile) or, at t = T, the rank's
+// count.  Each block rebuilds that table for itself (no shared scratch, so
+// ranges on different streams never race) and each wave finds its segment
+// by binary search.
+
+struct RangeArgs {
+    const int32_t* rank_offset;
+    const int32_t* tile_base;  // column-major [C][ntiles]
+    const int32_t* col_total;  // [C]
+    int E, R, ntiles;
+    int tile0, tile1;          // tile index of t0; of t1, or -1 for t1 = T
+};
+
+__device__ __forceinline__ int range_prefix(const RangeArgs& g, int r, int tile)
+{
+    return tile < 0 ? g.col_total[g.E + r] : g.tile_base[(int64_t)(g.E + r) * g.ntiles + tile];
+}
+
+template <int U, bool FULL>
+__global__ __launch_bounds__(kBlock) void dispatch_fanout_range_kernel(const u32x4* __restrict__ src,
+                                                                       u32x4* __restrict__ dst,
+                                                                       const int32_t* __restrict__ fan_dst, int D,
+                                                                       RangeArgs g, RowSplit rs,
+                                                                       const int32_t* __restrict__ status)
+{
+    extern __shared__ int s_tab[];  // start[R] then exclusive prefix of lengths [R + 1]
+    __shared__ int s_wsum[kWavesPerBlock];
+    if (status[0] != MOE_SHUFFLE_OK) return;
+    const int R = g.R;
+    int* s_start = s_tab;
+    int* s_pre = s_tab + R;
+    int carry = 0;
+    for (int r0 = 0; r0 < R; r0 += kBlock) {
+        const int r = r0 + (int)threadIdx.x;
+        int len = 0;
+        if (r < R) {
+            const int a = range_prefix(g, r, g.tile0);
+            const int b = range_prefix(g, r, g.tile1);
+            s_start[r] = g.rank_offset[r] + a;
+            len = b - a;
+        }
+        int total;
+        const int incl = block_inclusive_scan(len, s_wsum, &total);
+        if (r < R) s_pre[r] = carry + incl - len;
+        carry += total;
+    }
+    if (threadIdx.x == 0) s_pre[R] = carry;
+    __syncthreads();
+
+    const int wave = wave_id(), lane = lane_id();
+    const int u = (int)blockIdx.x * kWavesPerBlock + wave;
+    const int l = fdiv(u, rs.div);
+    if (l >= carry) return;
+    int lo = 0, hi = R - 1;  // largest r with s_pre[r] <= l
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pre[mid] <= l) lo = mid;
+        else hi = mid - 1;
+    }
+    const int p = __builtin_amdgcn_readfirstlane(s_start[lo] + (l - s_pre[lo]));
+    const int V = rs.V;
+    const int c0 = (u - l * rs.cpr) * (kWave * U);
+    const u32x4* sp = src + (int64_t)p * V + c0;
+    u32x4 v[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+        if (FULL || c0 + i * kWave + lane < V) v[i] = load_row16<MS_FANOUT_NT_LOAD>(sp + i * kWave + lane);
+    const int32_t* targets = fan_dst + (int64_t)p * D;
+    for (int d = 0; d < D; ++d) {
+        const int q = __builtin_amdgcn_readfirstlane(targets[d]);
+        if (q < 0) break;
+        u32x4* o = dst + (int64_t)q * V + c0;
+#pragma unroll
+        for (int i = 0; i < U; ++i)
+            if (FULL || c0 + i * kWave + lane < V) store_row16<MS_FANOUT_NT_STORE>(v[i], o + i * kWave + lane);
+    }
+}
+
+hipError_t launch_fanout_range(const void* xr, void* xe, const int32_t* fan_dst, int D, const int32_t* rank_offset,
+                               const int32_t* tile_base, const int32_t* col_total, int E, int R, int ntiles, int t0,
+                               int t1, int T, int KR, int H, const int32_t* status, hipStream_t s)
+{
+    if (t1 <= t0) return hipSuccess;
+    const int V = H / 8;
+    RowSplit rs;
+    const int64_t bound = (int64_t)(t1 - t0) * KR;  // each token reaches at most KR ranks
+    if (!make_split(V, 1, bound, &rs)) return hipErrorInvalidValue;
+    RangeArgs g;
+    g.rank_offset = rank_offset; g.tile_base = tile_base; g.col_total = col_total;
+    g.E = E; g.R = R; g.ntiles = ntiles;
+    g.tile0 = t0 / kPlanTile;
+    g.tile1 = t1 == T ? -1 : t1 / kPlanTile;
+    const dim3 grid(grid_for(bound * rs.cpr, kWavesPerBlock));
+    const size_t lds = sizeof(int) * (2 * (size_t)R + 1);
+    const u32x4* sp = (const u32x4*)xr;
+    u32x4* dp = (u32x4*)xe;
+    if (V % kWave == 0)
+        hipLaunchKernelGGL((dispatch_fanout_range_kernel<1, true>), grid, dim3(kBlock), lds, s, sp, dp, fan_dst, D, g,
+                           rs, status);
+    else
+        hipLaunchKernelGGL((dispatch_fanout_range_kernel<1, false>), grid, dim3(kBlock), lds, s, sp, dp, fan_dst, D,
+                           g, rs, status);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- reductions
@@ -585,7 +789,7 @@ __device__ __forceinline__ unsigned bf16_rne(float f)
 
 enum WeightMode { kUnweighted = 0, kPerSlot = 1, kPerSourceRow = 2 };
 
-template <int U, bool FULL, int WMODE, bool NTL, bool NTS>
+template <int U, bool FULL, int WMODE, bool NTL, bool NTS, int WPB, int MAXW>
 __device__ __forceinline__ void reduce_rows(int* s_tile, const u32x4* __restrict__ src,
                                             const int32_t* __restrict__ map, int width,
                                             const float* __restrict__ w, u32x4* __restrict__ out, int64_t n_bound,
@@ -594,19 +798,20 @@ __device__ __forceinline__ void reduce_rows(int* s_tile, const u32x4* __restrict
 {
     if (status[0] != MOE_SHUFFLE_OK) return;
     const int64_t n = n_dev ? (int64_t)n_dev[0] : n_bound;
+    const int u0 = block_first_unit<WPB>(n_dev != nullptr);
     int first, count;
-    block_rows(n, rs, &first, &count);
+    block_rows<WPB>(u0, n, rs, &first, &count);
     if (count <= 0) return;
     int* s_rows = s_tile;                               // [rows of this block][width]
-    int* s_w = s_tile + kWavesPerBlock * width;         // per-slot gates, same shape
-    for (int i = threadIdx.x; i < count * width; i += kBlock) {
+    int* s_w = s_tile + WPB * width;                    // per-slot gates, same shape
+    for (int i = threadIdx.x; i < count * width; i += WPB * kWave) {
         s_rows[i] = map[(int64_t)first * width + i];
         if (WMODE == kPerSlot) s_w[i] = __float_as_int(w[(int64_t)first * width + i]);
     }
     __syncthreads();
 
     const int wave = wave_id(), lane = lane_id();
-    const int u = (int)blockIdx.x * kWavesPerBlock + wave;
+    const int u = u0 + wave;
     const int row = fdiv(u, rs.div);
     if (row >= n) return;
     const int V = rs.V;
@@ -619,23 +824,79 @@ __device__ __forceinline__ void reduce_rows(int* s_tile, const u32x4* __restrict
     for (int i = 0; i < U; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
-    for (int j = 0; j < width; ++j) {
-        const int q = __builtin_amdgcn_readfirstlane(trow[j]);
-        if (q < 0) break;
-        float wj = 1.0f;
-        if (WMODE == kPerSlot) wj = __int_as_float(__builtin_amdgcn_readfirstlane(tw[j]));
-        if (WMODE == kPerSourceRow) wj = w[q];
-        const u32x4* y = src + (int64_t)q * V + c0;
+    // Terms in groups of G: the group's row indices first, then all its
+    // loads back to back (G KiB in flight per wave instead of one), then the
+    // fused multiply-adds in ascending term order.  A -1 ends the map row.
+    // With MAXW <= G the term loop is one straight-line group (no back edge),
+    // which lets every load of the group be in flight at once.  Whole-row
+    // units (U = 8) already carry 8 KiB per term and keep a plain loop: an
+    // unrolled one hoists the next term's loads and the extra registers cost
+    // more occupancy than they buy.
+    constexpr int G = U >= 8 ? 1 : 8 / U;
+    if constexpr (G == 1) {
+#pragma unroll 1
+        for (int j = 0; j < width; ++j) {
+            const int q = __builtin_amdgcn_readfirstlane(trow[j]);
+            if (q < 0) break;
+            float wj = 1.0f;
+            if (WMODE == kPerSlot) wj = __int_as_float(__builtin_amdgcn_readfirstlane(tw[j]));
+            if (WMODE == kPerSourceRow) wj = w[q];
+            const u32x4* y = src + (int64_t)q * V + c0;
 #pragma unroll
-        for (int i = 0; i < U; ++i) {
-            if (FULL || c0 + i * kWave + lane < V) {
-                const u32x4 v = load_row16<NTL>(y + i * kWave + lane);
+            for (int i = 0; i < U; ++i) {
+                if (FULL || c0 + i * kWave + lane < V) {
+                    const u32x4 vv = load_row16<NTL>(y + i * kWave + lane);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc[i][2 * e] = __builtin_fmaf(wj, __uint_as_float(v[e] << 16), acc[i][2 * e]);
-                    acc[i][2 * e + 1] = __builtin_fmaf(wj, __uint_as_float(v[e] & 0xffff0000u), acc[i][2 * e + 1]);
+                    for (int e = 0; e < 4; ++e) {
+                        acc[i][2 * e] = __builtin_fmaf(wj, __uint_as_float(vv[e] << 16), acc[i][2 * e]);
+                        acc[i][2 * e + 1] =
+                            __builtin_fmaf(wj, __uint_as_float(vv[e] & 0xffff0000u), acc[i][2 * e + 1]);
+                    }
+                }
+                // one 1 KiB piece at a time keeps registers (and occupancy) at
+                // their best for whole-row units
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    bool ended = G == 1;
+#pragma unroll
+    for (int j0 = 0; j0 < (MAXW <= G ? G : MAXW); j0 += G) {
+        if (!ended && j0 < width) {
+            int q[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                q[g] = (j0 + g < width) ? __builtin_amdgcn_readfirstlane(trow[j0 + g]) : -1;
+            u32x4 v[G][U];
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                if (q[g] >= 0) {
+                    const u32x4* y = src + (int64_t)q[g] * V + c0;
+#pragma unroll
+                    for (int i = 0; i < U; ++i)
+                        if (FULL || c0 + i * kWave + lane < V) v[g][i] = load_row16<NTL>(y + i * kWave + lane);
+                }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (q[g] >= 0) {
+                    float wj = 1.0f;
+                    if (WMODE == kPerSlot) wj = __int_as_float(__builtin_amdgcn_readfirstlane(tw[j0 + g]));
+                    if (WMODE == kPerSourceRow) wj = w[q[g]];
+#pragma unroll
+                    for (int i = 0; i < U; ++i) {
+                        if (FULL || c0 + i * kWave + lane < V) {
+                            const u32x4 vv = v[g][i];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                acc[i][2 * e] = __builtin_fmaf(wj, __uint_as_float(vv[e] << 16), acc[i][2 * e]);
+                                acc[i][2 * e + 1] =
+                                    __builtin_fmaf(wj, __uint_as_float(vv[e] & 0xffff0000u), acc[i][2 * e + 1]);
+                            }
+                        }
+                    }
                 }
             }
+            ended = q[G - 1] < 0;  // a -1 ends the map row; all later entries are -1 too
         }
     }
     u32x4* o = out + (int64_t)row * V + c0;
@@ -651,21 +912,23 @@ __device__ __forceinline__ void reduce_rows(int* s_tile, const u32x4* __restrict
 }
 
 #define MS_REDUCE_KERNEL(NAME, NTL, NTS)                                                                         \
-    template <int U, bool FULL, int WMODE>                                                                       \
-    __global__ __launch_bounds__(kBlock) void NAME(const u32x4* __restrict__ src, const int32_t* __restrict__ map, \
-                                                   int width, const float* __restrict__ w, u32x4* __restrict__ out, \
-                                                   int64_t n_bound, const int32_t* __restrict__ n_dev, RowSplit rs, \
-                                                   const int32_t* __restrict__ status)                            \
+    template <int U, bool FULL, int WMODE, int WPB, int MAXW>                                                    \
+    __global__ __launch_bounds__(WPB * kWave) void NAME(const u32x4* __restrict__ src,                           \
+                                                        const int32_t* __restrict__ map, int width,             \
+                                                        const float* __restrict__ w, u32x4* __restrict__ out,   \
+                                                        int64_t n_bound, const int32_t* __restrict__ n_dev,     \
+                                                        RowSplit rs, const int32_t* __restrict__ status)        \
     {                                                                                                            \
         extern __shared__ int s_tile[];                                                                          \
-        reduce_rows<U, FULL, WMODE, NTL, NTS>(s_tile, src, map, width, w, out, n_bound, n_dev, rs, status);      \
+        reduce_rows<U, FULL, WMODE, NTL, NTS, WPB, MAXW>(s_tile, src, map, width, w, out, n_bound, n_dev, rs,    \
+                                                         status);                                                \
     }
 // ye (expert-major) -> out (token-major): the forward combine.
 MS_REDUCE_KERNEL(combine_rows_kernel, MS_COMBINE_NT_LOAD, MS_COMBINE_NT_STORE)
 // expert-major rows -> one row per (token, rank): the receiver's sum.
-MS_REDUCE_KERNEL(sum_expert_rows_kernel, MS_COMBINE_NT_LOAD, MS_COMBINE_NT_STORE)
+MS_REDUCE_KERNEL(sum_expert_rows_kernel, MS_SUMX_NT_LOAD, MS_SUMX_NT_STORE)
 // rank-major rows -> one row per token: the sender's sum.
-MS_REDUCE_KERNEL(sum_rank_rows_kernel, MS_COMBINE_NT_LOAD, MS_COMBINE_NT_STORE)
+MS_REDUCE_KERNEL(sum_rank_rows_kernel, MS_SUMR_NT_LOAD, MS_SUMR_NT_STORE)
 #undef MS_REDUCE_KERNEL
 
 // Gathers from a large buffer use whole-row units: past a few GiB of
@@ -679,45 +942,74 @@ MS_REDUCE_KERNEL(sum_rank_rows_kernel, MS_COMBINE_NT_LOAD, MS_COMBINE_NT_STORE)
 #define MS_COMBINE_LARGE_BYTES (2ll << 30)
 #endif
 
-static int reduce_unit(int V, int64_t src_bytes)
+#ifndef MS_SUMX_UNIT
+#define MS_SUMX_UNIT 2  // measured: 279 us against 338 us at U = 1 (DeepSeek-V3-like)
+#endif
+#ifndef MS_SUMR_UNIT
+#define MS_SUMR_UNIT 1
+#endif
+
+static int reduce_unit(int kind, int V, int64_t src_bytes)
 {
-    return fit_unit(V, src_bytes > (int64_t)MS_COMBINE_LARGE_BYTES ? MS_COMBINE_UNIT_LARGE : MS_COMBINE_UNIT);
+    const bool large = src_bytes > (int64_t)MS_COMBINE_LARGE_BYTES;
+    const int small_unit = kind == 1 ? MS_SUMX_UNIT : kind == 2 ? MS_SUMR_UNIT : MS_COMBINE_UNIT;
+    return fit_unit(V, large ? MS_COMBINE_UNIT_LARGE : small_unit);
 }
 
 enum ReduceKind { kCombine = 0, kSumExpertRows = 1, kSumRankRows = 2 };
 
-template <int KIND, int U, bool FULL, int WMODE>
+template <int KIND, int U, bool FULL, int WMODE, int WPB, int MAXW>
 static void launch_reduce_kernel(dim3 grid, size_t lds, hipStream_t s, const u32x4* src, const int32_t* map,
                                  int width, const float* w, u32x4* out, int64_t n_bound, const int32_t* n_dev,
                                  RowSplit rs, const int32_t* status)
 {
-    if (KIND == kCombine)
-        hipLaunchKernelGGL((combine_rows_kernel<U, FULL, WMODE>), grid, dim3(kBlock), lds, s, src, map, width, w, out,
-                           n_bound, n_dev, rs, status);
-    else if (KIND == kSumExpertRows)
-        hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE>), grid, dim3(kBlock), lds, s, src, map, width, w,
+    const dim3 block(WPB * kWave);
+    if constexpr (KIND == kCombine)
+        hipLaunchKernelGGL((combine_rows_kernel<U, FULL, WMODE, WPB, MAXW>), grid, block, lds, s, src, map, width, w,
                            out, n_bound, n_dev, rs, status);
+    else if constexpr (KIND == kSumExpertRows)
+        hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW>), grid, block, lds, s, src, map, width,
+                           w, out, n_bound, n_dev, rs, status);
     else
-        hipLaunchKernelGGL((sum_rank_rows_kernel<U, FULL, WMODE>), grid, dim3(kBlock), lds, s, src, map, width, w,
-                           out, n_bound, n_dev, rs, status);
+        hipLaunchKernelGGL((sum_rank_rows_kernel<U, FULL, WMODE, WPB, MAXW>), grid, block, lds, s, src, map, width,
+                           w, out, n_bound, n_dev, rs, status);
+}
+
+template <int KIND, int WMODE, int U, int WPB>
+static hipError_t launch_reduce_uw(const void* src, const int32_t* map, int width, const float* w, void* out,
+                                   int64_t n_bound, const int32_t* n_dev, int V, const int32_t* status, hipStream_t s)
+{
+    RowSplit rs;
+    if (!make_split(V, U, n_bound, &rs)) return hipErrorInvalidValue;
+    const dim3 grid(grid_for(n_bound * rs.cpr, WPB));
+    const size_t lds = tile_lds_bytes(width, 2, WPB);
+    const u32x4* sp = (const u32x4*)src;
+    u32x4* op = (u32x4*)out;
+    const bool full = V % (kWave * U) == 0;
+    if (width <= 8 && full)
+        launch_reduce_kernel<KIND, U, true, WMODE, WPB, 8>(grid, lds, s, sp, map, width, w, op, n_bound, n_dev, rs,
+                                                           status);
+    else if (width <= 8)
+        launch_reduce_kernel<KIND, U, false, WMODE, WPB, 8>(grid, lds, s, sp, map, width, w, op, n_bound, n_dev, rs,
+                                                            status);
+    else if (full)
+        launch_reduce_kernel<KIND, U, true, WMODE, WPB, kMaxTopK>(grid, lds, s, sp, map, width, w, op, n_bound,
+                                                                  n_dev, rs, status);
+    else
+        launch_reduce_kernel<KIND, U, false, WMODE, WPB, kMaxTopK>(grid, lds, s, sp, map, width, w, op, n_bound,
+                                                                   n_dev, rs, status);
+    return hipGetLastError();
 }
 
 template <int KIND, int WMODE, int U>
 static hipError_t launch_reduce_u(const void* src, const int32_t* map, int width, const float* w, void* out,
                                   int64_t n_bound, const int32_t* n_dev, int V, const int32_t* status, hipStream_t s)
 {
-    RowSplit rs;
-    if (!make_split(V, U, n_bound, &rs)) return hipErrorInvalidValue;
-    const int64_t units = n_bound * rs.cpr;
-    const dim3 grid((unsigned)((units + kWavesPerBlock - 1) / kWavesPerBlock));
-    const size_t lds = tile_lds_bytes(width, 2);
-    const u32x4* sp = (const u32x4*)src;
-    u32x4* op = (u32x4*)out;
-    if (V % (kWave * U) == 0)
-        launch_reduce_kernel<KIND, U, true, WMODE>(grid, lds, s, sp, map, width, w, op, n_bound, n_dev, rs, status);
-    else
-        launch_reduce_kernel<KIND, U, false, WMODE>(grid, lds, s, sp, map, width, w, op, n_bound, n_dev, rs, status);
-    return hipGetLastError();
+    if constexpr (U <= 2) {
+        if (n_dev)
+            return launch_reduce_uw<KIND, WMODE, U, kWavesBig>(src, map, width, w, out, n_bound, n_dev, V, status, s);
+    }
+    return launch_reduce_uw<KIND, WMODE, U, kWavesPerBlock>(src, map, width, w, out, n_bound, n_dev, V, status, s);
 }
 
 template <int KIND, int WMODE>
@@ -727,7 +1019,7 @@ static hipError_t launch_reduce(const void* src, int64_t src_rows, const int32_t
 {
     if (n_bound <= 0) return hipSuccess;
     const int V = H / 8;
-    switch (reduce_unit(V, src_rows * (int64_t)H * 2)) {
+    switch (reduce_unit(KIND, V, src_rows * (int64_t)H * 2)) {
         case 1: return launch_reduce_u<KIND, WMODE, 1>(src, map, width, w, out, n_bound, n_dev, V, status, s);
         case 2: return launch_reduce_u<KIND, WMODE, 2>(src, map, width, w, out, n_bound, n_dev, V, status, s);
         case 4: return launch_reduce_u<KIND, WMODE, 4>(src, map, width, w, out, n_bound, n_dev, V, status, s);
@@ -797,7 +1089,7 @@ __global__ __launch_bounds__(kBlock) void combine_bwd_kernel(const u32x4* __rest
     extern __shared__ int s_tile[];
     if (status[0] != MOE_SHUFFLE_OK) return;
     int first, count;
-    block_rows(T, rs, &first, &count);
+    block_rows<kWavesPerBlock>((int)blockIdx.x * kWavesPerBlock, T, rs, &first, &count);
     if (count <= 0) return;
     int* s_rows = s_tile;
     int* s_w = s_tile + kWavesPerBlock * k;
@@ -817,42 +1109,68 @@ __global__ __launch_bounds__(kBlock) void combine_bwd_kernel(const u32x4* __rest
     const int* trow = s_rows + (t - first) * k;
     const int* tw = s_w + (t - first) * k;
 
-    float g[U][8];
+    float g_[U][8];  // this chunk of grad_out
     const u32x4* gp = grad_out + (int64_t)t * V + c0;
 #pragma unroll
     for (int i = 0; i < U; ++i) {
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (FULL || c0 + i * kWave + lane < V) v = load_row16<MS_COMBINE_NT_LOAD>(gp + i * kWave + lane);
+        if (FULL || c0 + i * kWave + lane < V) v = load_row16<MS_CBWD_NT_LOAD>(gp + i * kWave + lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            g[i][2 * e] = __uint_as_float(v[e] << 16);
-            g[i][2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+            g_[i][2 * e] = __uint_as_float(v[e] << 16);
+            g_[i][2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
         }
     }
     float mine = 0.0f;  // lane j keeps slot j's chunk total
-    for (int j = 0; j < k; ++j) {
-        const int q = __builtin_amdgcn_readfirstlane(trow[j]);
-        const float wj = __int_as_float(__builtin_amdgcn_readfirstlane(tw[j]));
-        const u32x4* y = ye + (int64_t)q * V + c0;
-        u32x4* gy = grad_ye + (int64_t)q * V + c0;
-        float part = 0.0f;
+    constexpr int G = U >= 8 ? 1 : 8 / U;
+    for (int j0 = 0; j0 < k; j0 += G) {
+        // the group's ye loads back to back, then products and gate-gradient partials
+        int q[G];
+        float wj[G];
 #pragma unroll
-        for (int i = 0; i < U; ++i) {
-            if (FULL || c0 + i * kWave + lane < V) {
-                const u32x4 v = load_row16<MS_COMBINE_NT_LOAD>(y + i * kWave + lane);
-                u32x4 pk;
+        for (int g = 0; g < G; ++g) {
+            q[g] = (j0 + g < k) ? __builtin_amdgcn_readfirstlane(trow[j0 + g]) : -1;
+            wj[g] = (j0 + g < k) ? __int_as_float(__builtin_amdgcn_readfirstlane(tw[j0 + g])) : 0.0f;
+        }
+        u32x4 v[G][U];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    part = __builtin_fmaf(g[i][2 * e], __uint_as_float(v[e] << 16), part);
-                    part = __builtin_fmaf(g[i][2 * e + 1], __uint_as_float(v[e] & 0xffff0000u), part);
-                    pk[e] = bf16_rne(__fmul_rn(wj, g[i][2 * e])) | (bf16_rne(__fmul_rn(wj, g[i][2 * e + 1])) << 16);
+        for (int g = 0; g < G; ++g)
+            if (q[g] >= 0) {
+                const u32x4* y = ye + (int64_t)q[g] * V + c0;
+#pragma unroll
+                for (int i = 0; i < U; ++i)
+                    if (FULL || c0 + i * kWave + lane < V) v[g][i] = load_row16<MS_CBWD_NT_LOAD>(y + i * kWave + lane);
+            }
+        float part[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            part[g] = 0.0f;
+            if (q[g] < 0) continue;
+            u32x4* gy = grad_ye + (int64_t)q[g] * V + c0;
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                if (FULL || c0 + i * kWave + lane < V) {
+                    const u32x4 vv = v[g][i];
+                    u32x4 pk;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        part[g] = __builtin_fmaf(g_[i][2 * e], __uint_as_float(vv[e] << 16), part[g]);
+                        part[g] = __builtin_fmaf(g_[i][2 * e + 1], __uint_as_float(vv[e] & 0xffff0000u), part[g]);
+                        pk[e] = bf16_rne(__fmul_rn(wj[g], g_[i][2 * e])) |
+                                (bf16_rne(__fmul_rn(wj[g], g_[i][2 * e + 1])) << 16);
+                    }
+                    store_row16<MS_CBWD_NT_STORE>(pk, gy + i * kWave + lane);
                 }
-                store_row16<MS_COMBINE_NT_STORE>(pk, gy + i * kWave + lane);
             }
         }
 #pragma unroll
-        for (int m = kWave / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
-        if (lane == j) mine = part;
+        for (int g = 0; g < G; ++g) {
+            if (j0 + g >= k) break;
+            float x = part[g];
+#pragma unroll
+            for (int m = kWave / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+            if (lane == j0 + g) mine = x;
+        }
     }
     if (lane < k) dots[((int64_t)t * rs.cpr + chunk) * k + lane] = mine;
 }
@@ -879,9 +1197,8 @@ static hipError_t launch_combine_bwd_u(const void* grad_out, const void* ye, con
 {
     RowSplit rs;
     if (!make_split(V, U, T, &rs)) return hipErrorInvalidValue;
-    const int64_t units = (int64_t)T * rs.cpr;
-    const dim3 grid((unsigned)((units + kWavesPerBlock - 1) / kWavesPerBlock));
-    const size_t lds = tile_lds_bytes(k, 2);
+    const dim3 grid(grid_for((int64_t)T * rs.cpr, kWavesPerBlock));
+    const size_t lds = tile_lds_bytes(k, 2, kWavesPerBlock);
     const u32x4* gp = (const u32x4*)grad_out;
     const u32x4* yp = (const u32x4*)ye;
     u32x4* gyp = (u32x4*)grad_ye;

@@ -783,8 +783,37 @@ hipError_t launch_fanout_range(const void* xr, void* xe, const int32_t* fan_dst,
 __device__ __forceinline__ unsigned bf16_rne(float f)
 {
     const unsigned u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const unsigned rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const unsigned quiet_nan = (u >> 16) | 0x40u;
+    return (u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded;  // a select, not a branch
+}
+
+// Sum of p[s] over the 64 lanes for the 8 slots s, scattered: lane l ends
+// with the total of slot s(l) = 4*bit5(l) + 2*bit4(l) + bit3(l).  Each step
+// halves the values a lane carries (10 shuffles in all instead of 48); every
+// slot's total is the same fixed 6-level pairwise tree in every lane.
+__device__ __forceinline__ float reduce_scatter8(const float p[8], int lane)
+{
+    const bool h5 = (lane & 32) != 0, h4 = (lane & 16) != 0, h3 = (lane & 8) != 0;
+    float a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float keep = h5 ? p[i + 4] : p[i];
+        const float send = h5 ? p[i] : p[i + 4];
+        a[i] = keep + __shfl_xor(send, 32, kWave);
+    }
+    float b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float keep = h4 ? a[i + 2] : a[i];
+        const float send = h4 ? a[i] : a[i + 2];
+        b[i] = keep + __shfl_xor(send, 16, kWave);
+    }
+    float c = (h3 ? b[1] : b[0]) + __shfl_xor(h3 ? b[0] : b[1], 8, kWave);
+    c += __shfl_xor(c, 4, kWave);
+    c += __shfl_xor(c, 2, kWave);
+    c += __shfl_xor(c, 1, kWave);
+    return c;
 }
 
 enum WeightMode { kUnweighted = 0, kPerSlot = 1, kPerSourceRow = 2 };
@@ -1074,7 +1103,8 @@ hipError_t launch_sum_rank_rows(const void* src, int64_t src_rows, const int32_t
 // One wave per 64*U-vector chunk of a token's row: the chunk of grad_out is
 // loaded once and reused for all k slots.  The gate gradient is summed in a
 // fixed order: each lane over its elements (ascending h), a butterfly over
-// the 64 lanes, then (second kernel) the chunks of a row in ascending order.
+// the 64 lanes (one 6-level tree per slot), then (second kernel) the chunks
+// of a row in ascending order.
 // Each bf16 x bf16 product is exact in fp32.
 
 template <int U, bool FULL>
@@ -1121,8 +1151,7 @@ __global__ __launch_bounds__(kBlock) void combine_bwd_kernel(const u32x4* __rest
             g_[i][2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
         }
     }
-    float mine = 0.0f;  // lane j keeps slot j's chunk total
-    constexpr int G = U >= 8 ? 1 : 8 / U;
+    constexpr int G = 8;  // slots per group: one reduce-scatter per group
     for (int j0 = 0; j0 < k; j0 += G) {
         // the group's ye loads back to back, then products and gate-gradient partials
         int q[G];
@@ -1163,16 +1192,10 @@ __global__ __launch_bounds__(kBlock) void combine_bwd_kernel(const u32x4* __rest
                 }
             }
         }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if (j0 + g >= k) break;
-            float x = part[g];
-#pragma unroll
-            for (int m = kWave / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
-            if (lane == j0 + g) mine = x;
-        }
+        const float total = reduce_scatter8(part, lane);
+        const int slot = j0 + 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
+        if ((lane & 7) == 0 && slot < k) dots[((int64_t)t * rs.cpr + chunk) * k + slot] = total;
     }
-    if (lane < k) dots[((int64_t)t * rs.cpr + chunk) * k + lane] = mine;
 }
 
 // grad_w[t][j] = sum over chunks c (ascending) of dots[t][c][j].

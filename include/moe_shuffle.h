@@ -176,7 +176,7 @@ int moe_shuffle_combine(moe_shuffle_plan_t plan, const void* ye, const float* to
  * Token ranges (DySHARP write-up, section 6 / Fig. 12: the shuffle runs per
  * group of tokens, so the dispatch of one group overlaps later stages of the
  * previous one).  Both calls act on the tokens [t0, t1) of the plan: t0 a
- * multiple of 256 (the plan's token tile), t1 a multiple of 256 or T.
+ * multiple of 64 (the plan's token tile), t1 a multiple of 64 or T.
  * Rows land exactly where the whole-batch calls put them: the rank rows of
  * the range are a contiguous sub-range of every rank segment, its expert
  * rows a contiguous sub-range of every expert segment.  Buffers are the

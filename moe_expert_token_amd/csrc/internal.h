@@ -13,7 +13,7 @@ namespace ms {
 constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kBlock = 256;        // threads per block for every kernel
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kPlanTile = kBlock;  // tokens per plan block (one per thread)
+constexpr int kPlanTile = kWave;   // tokens per plan tile: one wave, one lane per token
 constexpr int kMaxTopK = 64;
 constexpr int kMaxCols = 1024;     // E + R: histogram columns per token tile
 

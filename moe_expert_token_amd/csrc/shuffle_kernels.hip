@@ -2,16 +2,16 @@
 //
 // Plan (FUSCO abstract: the light-weight planner that drops redundant
 // sends; press summary, Group 3: logical segments):
-//   plan_count  one block per 256-token tile; every wave ORs its lanes'
-//               bits into one 64-bit LDS mask per expert and per rank, so a
-//               token with several experts on one rank sets that rank's bit
-//               once (the send-once rule) and no result depends on the
-//               order of the atomics.  Counts are popcounts of the masks.
+//   plan_count  one wave per 64-token tile; the wave ORs its lanes' bits
+//               into one 64-bit LDS mask per expert and per rank, so a token
+//               with several experts on one rank sets that rank's bit once
+//               (the send-once rule) and no result depends on the order of
+//               the atomics.  Counts are popcounts of the masks.
 //   plan_scan   one block per histogram column: wavefront-level exclusive
 //               scan over the tiles.
 //   plan_place  recomputes the masks, scans the column totals into
 //               offsets, and gives every (token, rank) and (token, expert)
-//               pair its row: tile base + earlier waves + mbcnt(mask).  Rows
+//               pair its row: tile base + mbcnt(mask).  Rows
 //               come out in ascending token order inside every segment.
 // Data movement (HBM bound, no MFMA: nothing here is a contraction):
 //   fanout_rows   each source row is read once, 16 bytes per lane, and
@@ -91,17 +91,37 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* s_wsum, int* tot
 
 // ---------------------------------------------------------------- plan_count
 
-// hist is column-major [(C+1)][ntiles]; column C holds the tile's error flag.
-template <int KMAX>
-__global__ __launch_bounds__(kBlock) void plan_count_kernel(const int32_t* __restrict__ idx, int T, int k,
-                                                            int E, FastDiv epr, int C, int ntiles,
-                                                            int32_t* __restrict__ hist)
+// Sum over the wave (every lane gets it).
+__device__ __forceinline__ int wave_sum(int v)
 {
-    extern __shared__ unsigned long long s_mask[];  // [4][C]
-    __shared__ int s_slots, s_ecount;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+// Inclusive scan over the wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int n = __shfl_up(v, d, kWave);
+        if (lane >= d) v += n;
+    }
+    return v;
+}
+
+// One wave per 64-token tile.  hist is column-major [(C+1)][ntiles];
+// column C holds the tile's error flag.
+template <int KMAX>
+__global__ __launch_bounds__(kWave) void plan_count_kernel(const int32_t* __restrict__ idx, int T, int k,
+                                                           int E, FastDiv epr, int C, int ntiles,
+                                                           int32_t* __restrict__ hist)
+{
+    extern __shared__ unsigned long long s_mask[];  // [C]
+    const int lane = threadIdx.x;
     const int tile = blockIdx.x;
-    const int t = tile * kPlanTile + tid;
+    const int t = tile * kPlanTile + lane;
 
     // The ids first (their load overlaps the clearing of the masks).
     int ev[KMAX];
@@ -113,14 +133,12 @@ __global__ __launch_bounds__(kBlock) void plan_count_kernel(const int32_t* __res
         for (int j = 0; j < KMAX; ++j)
             if (j < k) ev[j] = row[j];
     }
-    if (tid == 0) { s_slots = 0; s_ecount = 0; }
-    for (int i = tid; i < kWavesPerBlock * C; i += kBlock) s_mask[i] = 0ull;
+    for (int i = lane; i < C; i += kWave) s_mask[i] = 0ull;
     __syncthreads();
 
     int bad = 0, nslots = 0;
     if (t < T) {
         const unsigned long long bit = 1ull << lane;
-        unsigned long long* m = s_mask + wave * C;
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
             if (j < k) {
@@ -129,28 +147,25 @@ __global__ __launch_bounds__(kBlock) void plan_count_kernel(const int32_t* __res
                     bad = 1;
                 } else {
                     ++nslots;
-                    atomicOr(&m[e], bit);
-                    atomicOr(&m[E + fdiv(e, epr)], bit);
+                    atomicOr(&s_mask[e], bit);
+                    atomicOr(&s_mask[E + fdiv(e, epr)], bit);
                 }
             }
         }
     }
-    if (nslots) atomicAdd(&s_slots, nslots);
-    bad = __syncthreads_or(bad);
+    __syncthreads();
 
     int ecount = 0;
-    for (int c = tid; c < C; c += kBlock) {
-        int cnt = 0;
-#pragma unroll
-        for (int w = 0; w < kWavesPerBlock; ++w) cnt += __popcll(s_mask[w * C + c]);
+    for (int c = lane; c < C; c += kWave) {
+        const int cnt = __popcll(s_mask[c]);
         hist[(int64_t)c * ntiles + tile] = cnt;
         if (c < E) ecount += cnt;
     }
-    if (ecount) atomicAdd(&s_ecount, ecount);
-    __syncthreads();
     // A token that names one expert twice sets that expert's bit once, so
     // the expert popcounts fall short of the in-range slots.
-    if (tid == 0) hist[(int64_t)C * ntiles + tile] = (bad || s_ecount != s_slots) ? 1 : 0;
+    const bool any_bad = __ballot(bad) != 0ull;
+    const int slots = wave_sum(nslots), placed = wave_sum(ecount);
+    if (lane == 0) hist[(int64_t)C * ntiles + tile] = (any_bad || placed != slots) ? 1 : 0;
 }
 
 // ---------------------------------------------------------------- plan_scan
@@ -200,23 +215,21 @@ struct PlaceArgs {
 };
 
 template <int KMAX>
-__global__ __launch_bounds__(kBlock) void plan_place_kernel(PlaceArgs a)
+__global__ __launch_bounds__(kWave) void plan_place_kernel(PlaceArgs a)
 {
     extern __shared__ unsigned long long s_dyn[];
     const int C = a.C, E = a.E, R = a.R;
-    unsigned long long* s_mask = s_dyn;                        // [4][C]
-    int* s_wbase = (int*)(s_mask + kWavesPerBlock * C);        // [4][C]
-    __shared__ int s_wsum[kWavesPerBlock];
-    __shared__ int s_etotal;
+    unsigned long long* s_mask = s_dyn;     // [C]
+    int* s_wbase = (int*)(s_mask + C);      // [C]
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lane = threadIdx.x;
     const int tile = blockIdx.x;
-    const int t = tile * kPlanTile + tid;
+    const int t = tile * kPlanTile + lane;
     const int k = a.k;
-    constexpr int kCols = kMaxCols / kBlock;  // histogram columns per thread
+    constexpr int kCols = kMaxCols / kWave;  // histogram columns per lane
 
     // Every global load first, so their latencies overlap: the status word,
-    // this thread's top-k ids, and for each column it owns the column total
+    // this lane's top-k ids, and for each column it owns the column total
     // and this tile's base within the column.
     const int status = a.status[0];
     int ev[KMAX];
@@ -231,74 +244,67 @@ __global__ __launch_bounds__(kBlock) void plan_place_kernel(PlaceArgs a)
     int ct[kCols], tb[kCols];
 #pragma unroll
     for (int i = 0; i < kCols; ++i) {
-        const int c = tid + i * kBlock;
+        const int c = lane + i * kWave;
         ct[i] = c < C ? a.col_total[c] : 0;
         tb[i] = c < C ? a.tile_base[(int64_t)c * a.ntiles + tile] : 0;
     }
 
-    for (int i = tid; i < kWavesPerBlock * C; i += kBlock) s_mask[i] = 0ull;
+    for (int i = lane; i < C; i += kWave) s_mask[i] = 0ull;
     __syncthreads();
     if (status != MOE_SHUFFLE_OK) return;
 
     // This tile's masks.
     if (t < a.T) {
         const unsigned long long bit = 1ull << lane;
-        unsigned long long* m = s_mask + wave * C;
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
             if (j < k) {
-                atomicOr(&m[ev[j]], bit);
-                atomicOr(&m[E + fdiv(ev[j], a.epr)], bit);
+                atomicOr(&s_mask[ev[j]], bit);
+                atomicOr(&s_mask[E + fdiv(ev[j], a.epr)], bit);
             }
     }
 
     // One exclusive scan over all columns, experts first then ranks; a rank
     // column's segment offset is its prefix minus the expert total.
     int excl[kCols];
-    int carry = 0;
+    int carry = 0, etot = 0;
 #pragma unroll
     for (int i = 0; i < kCols; ++i) {
-        if (i * kBlock >= C) break;  // uniform
-        int total;
-        const int incl = block_inclusive_scan(ct[i], s_wsum, &total);
-        excl[i] = carry + incl - ct[i];
-        carry += total;
+        excl[i] = 0;
+        if (i * kWave < C) {  // uniform
+            const int incl = wave_inclusive_scan(ct[i]);
+            excl[i] = carry + incl - ct[i];
+            carry += __shfl(incl, kWave - 1, kWave);
+            if (i == (E >> 6)) etot = __shfl(excl[i], E & (kWave - 1), kWave);  // uniform
+        }
     }
-#pragma unroll
-    for (int i = 0; i < kCols; ++i)
-        if (tid + i * kBlock == E) s_etotal = excl[i];
-    __syncthreads();
-    const int etot = s_etotal;
+    __syncthreads();  // the masks are complete
 
     // Segment offsets (tile 0 publishes them) and the first row of every
-    // column for each wave of this tile.
+    // column for this tile.
 #pragma unroll
     for (int i = 0; i < kCols; ++i) {
-        const int c = tid + i * kBlock;
-        if (c >= C) break;
-        const int off = c < E ? excl[i] : excl[i] - etot;
-        if (tile == 0) {
-            if (c < E) {
-                a.expert_count[c] = ct[i];
-                a.expert_offset[c] = off;
-                int32_t* seg = a.expert_segs + 4 * c;
-                seg[0] = fdiv(c, a.epr); seg[1] = c; seg[2] = off; seg[3] = ct[i];
-            } else {
-                const int r = c - E;
-                a.rank_count[r] = ct[i];
-                a.rank_offset[r] = off;
-                int32_t* seg = a.rank_segs + 4 * r;
-                seg[0] = r; seg[1] = -1; seg[2] = off; seg[3] = ct[i];
+        const int c = lane + i * kWave;
+        if (i * kWave < C && c < C) {
+            const int off = c < E ? excl[i] : excl[i] - etot;
+            if (tile == 0) {
+                if (c < E) {
+                    a.expert_count[c] = ct[i];
+                    a.expert_offset[c] = off;
+                    int32_t* seg = a.expert_segs + 4 * c;
+                    seg[0] = fdiv(c, a.epr); seg[1] = c; seg[2] = off; seg[3] = ct[i];
+                } else {
+                    const int r = c - E;
+                    a.rank_count[r] = ct[i];
+                    a.rank_offset[r] = off;
+                    int32_t* seg = a.rank_segs + 4 * r;
+                    seg[0] = r; seg[1] = -1; seg[2] = off; seg[3] = ct[i];
+                }
             }
-        }
-        int run = off + tb[i];
-#pragma unroll
-        for (int w = 0; w < kWavesPerBlock; ++w) {
-            s_wbase[w * C + c] = run;
-            run += __popcll(s_mask[w * C + c]);
+            s_wbase[c] = off + tb[i];
         }
     }
-    if (tile == 0 && tid == 0) {
+    if (tile == 0 && lane == 0) {
         a.expert_offset[E] = etot;
         a.rank_offset[R] = carry - etot;
         a.n_rank_rows[0] = carry - etot;
@@ -306,8 +312,8 @@ __global__ __launch_bounds__(kBlock) void plan_place_kernel(PlaceArgs a)
     __syncthreads();
     if (t >= a.T) return;
 
-    const unsigned long long* m = s_mask + wave * C;
-    const int* wb = s_wbase + wave * C;
+    const unsigned long long* m = s_mask;
+    const int* wb = s_wbase;
     const int KR = a.KR, D = a.D;
 
     // Expert row of every slot, in slot order.
@@ -361,19 +367,19 @@ __global__ __launch_bounds__(kBlock) void plan_place_kernel(PlaceArgs a)
 hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)
 {
     const int ntiles = L.ntiles;
-    const size_t lds_count = sizeof(unsigned long long) * kWavesPerBlock * L.C;
+    const size_t lds_count = sizeof(unsigned long long) * L.C;
     const FastDiv epr = make_fastdiv(L.Epr);
     if (L.k <= 8)
-        hipLaunchKernelGGL(plan_count_kernel<8>, dim3(ntiles), dim3(kBlock), lds_count, s, P.idx, L.T, L.k, L.E,
+        hipLaunchKernelGGL(plan_count_kernel<8>, dim3(ntiles), dim3(kWave), lds_count, s, P.idx, L.T, L.k, L.E,
                            epr, L.C, ntiles, P.tile_hist);
     else if (L.k <= 16)
-        hipLaunchKernelGGL(plan_count_kernel<16>, dim3(ntiles), dim3(kBlock), lds_count, s, P.idx, L.T, L.k, L.E,
+        hipLaunchKernelGGL(plan_count_kernel<16>, dim3(ntiles), dim3(kWave), lds_count, s, P.idx, L.T, L.k, L.E,
                            epr, L.C, ntiles, P.tile_hist);
     else if (L.k <= 32)
-        hipLaunchKernelGGL(plan_count_kernel<32>, dim3(ntiles), dim3(kBlock), lds_count, s, P.idx, L.T, L.k, L.E,
+        hipLaunchKernelGGL(plan_count_kernel<32>, dim3(ntiles), dim3(kWave), lds_count, s, P.idx, L.T, L.k, L.E,
                            epr, L.C, ntiles, P.tile_hist);
     else
-        hipLaunchKernelGGL(plan_count_kernel<64>, dim3(ntiles), dim3(kBlock), lds_count, s, P.idx, L.T, L.k, L.E,
+        hipLaunchKernelGGL(plan_count_kernel<64>, dim3(ntiles), dim3(kWave), lds_count, s, P.idx, L.T, L.k, L.E,
                            epr, L.C, ntiles, P.tile_hist);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -392,15 +398,15 @@ hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)
     a.send_token = P.send_token; a.tok_rank_row = P.tok_rank_row; a.fan_src = P.fan_src;
     a.fan_dst = P.fan_dst; a.comb_row = P.comb_row;
     a.rank_segs = P.rank_segs; a.expert_segs = P.expert_segs; a.n_rank_rows = P.n_rank_rows;
-    const size_t lds_place = lds_count + sizeof(int) * kWavesPerBlock * L.C;
+    const size_t lds_place = lds_count + sizeof(int) * L.C;
     if (L.k <= 8)
-        hipLaunchKernelGGL(plan_place_kernel<8>, dim3(ntiles), dim3(kBlock), lds_place, s, a);
+        hipLaunchKernelGGL(plan_place_kernel<8>, dim3(ntiles), dim3(kWave), lds_place, s, a);
     else if (L.k <= 16)
-        hipLaunchKernelGGL(plan_place_kernel<16>, dim3(ntiles), dim3(kBlock), lds_place, s, a);
+        hipLaunchKernelGGL(plan_place_kernel<16>, dim3(ntiles), dim3(kWave), lds_place, s, a);
     else if (L.k <= 32)
-        hipLaunchKernelGGL(plan_place_kernel<32>, dim3(ntiles), dim3(kBlock), lds_place, s, a);
+        hipLaunchKernelGGL(plan_place_kernel<32>, dim3(ntiles), dim3(kWave), lds_place, s, a);
     else
-        hipLaunchKernelGGL(plan_place_kernel<64>, dim3(ntiles), dim3(kBlock), lds_place, s, a);
+        hipLaunchKernelGGL(plan_place_kernel<64>, dim3(ntiles), dim3(kWave), lds_place, s, a);
     return hipGetLastError();
 }
 
@@ -1107,7 +1113,9 @@ hipError_t launch_sum_rank_rows(const void* src, int64_t src_rows, const int32_t
 // of a row in ascending order.
 // Each bf16 x bf16 product is exact in fp32.
 
-template <int U, bool FULL>
+// PART selects the work: 1 = grad_ye rows only, 2 = gate-gradient partials
+// only, 3 = both in one pass.
+template <int U, bool FULL, int PART>
 __global__ __launch_bounds__(kBlock) void combine_bwd_kernel(const u32x4* __restrict__ grad_out,
                                                              const u32x4* __restrict__ ye,
                                                              const float* __restrict__ w,
@@ -1164,7 +1172,7 @@ __global__ __launch_bounds__(kBlock) void combine_bwd_kernel(const u32x4* __rest
         u32x4 v[G][U];
 #pragma unroll
         for (int g = 0; g < G; ++g)
-            if (q[g] >= 0) {
+            if ((PART & 2) && q[g] >= 0) {
                 const u32x4* y = ye + (int64_t)q[g] * V + c0;
 #pragma unroll
                 for (int i = 0; i < U; ++i)
@@ -1179,22 +1187,30 @@ __global__ __launch_bounds__(kBlock) void combine_bwd_kernel(const u32x4* __rest
 #pragma unroll
             for (int i = 0; i < U; ++i) {
                 if (FULL || c0 + i * kWave + lane < V) {
-                    const u32x4 vv = v[g][i];
-                    u32x4 pk;
+                    if constexpr ((PART & 2) != 0) {
+                        const u32x4 vv = v[g][i];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        part[g] = __builtin_fmaf(g_[i][2 * e], __uint_as_float(vv[e] << 16), part[g]);
-                        part[g] = __builtin_fmaf(g_[i][2 * e + 1], __uint_as_float(vv[e] & 0xffff0000u), part[g]);
-                        pk[e] = bf16_rne(__fmul_rn(wj[g], g_[i][2 * e])) |
-                                (bf16_rne(__fmul_rn(wj[g], g_[i][2 * e + 1])) << 16);
+                        for (int e = 0; e < 4; ++e) {
+                            part[g] = __builtin_fmaf(g_[i][2 * e], __uint_as_float(vv[e] << 16), part[g]);
+                            part[g] = __builtin_fmaf(g_[i][2 * e + 1], __uint_as_float(vv[e] & 0xffff0000u), part[g]);
+                        }
                     }
-                    store_row16<MS_CBWD_NT_STORE>(pk, gy + i * kWave + lane);
+                    if constexpr ((PART & 1) != 0) {
+                        u32x4 pk;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            pk[e] = bf16_rne(__fmul_rn(wj[g], g_[i][2 * e])) |
+                                    (bf16_rne(__fmul_rn(wj[g], g_[i][2 * e + 1])) << 16);
+                        store_row16<MS_CBWD_NT_STORE>(pk, gy + i * kWave + lane);
+                    }
                 }
             }
         }
-        const float total = reduce_scatter8(part, lane);
-        const int slot = j0 + 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
-        if ((lane & 7) == 0 && slot < k) dots[((int64_t)t * rs.cpr + chunk) * k + slot] = total;
+        if constexpr ((PART & 2) != 0) {
+            const float total = reduce_scatter8(part, lane);
+            const int slot = j0 + 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
+            if ((lane & 7) == 0 && slot < k) dots[((int64_t)t * rs.cpr + chunk) * k + slot] = total;
+        }
     }
 }
 
@@ -1213,6 +1229,13 @@ __global__ __launch_bounds__(kBlock) void gate_grad_kernel(const float* __restri
     grad_w[i] = acc;
 }
 
+#ifndef MS_CBWD_SPLIT
+#define MS_CBWD_SPLIT 0
+#endif
+#ifndef MS_CBWD_UNIT
+#define MS_CBWD_UNIT 1
+#endif
+
 template <int U>
 static hipError_t launch_combine_bwd_u(const void* grad_out, const void* ye, const float* w, const int32_t* comb_row,
                                        void* grad_ye, float* grad_w, float* dots, int T, int k, int V,
@@ -1225,14 +1248,32 @@ static hipError_t launch_combine_bwd_u(const void* grad_out, const void* ye, con
     const u32x4* gp = (const u32x4*)grad_out;
     const u32x4* yp = (const u32x4*)ye;
     u32x4* gyp = (u32x4*)grad_ye;
-    if (V % (kWave * U) == 0)
-        hipLaunchKernelGGL((combine_bwd_kernel<U, true>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp, dots,
-                           T, k, rs, status);
-    else
-        hipLaunchKernelGGL((combine_bwd_kernel<U, false>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
-                           dots, T, k, rs, status);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    constexpr int parts[2][2] = {{3, 0}, {1, 2}};
+    for (int pass = 0; pass < 2; ++pass) {
+        const int part = parts[MS_CBWD_SPLIT][pass];
+        if (part == 0) break;
+        const bool full = V % (kWave * U) == 0;
+        if (part == 3 && full)
+            hipLaunchKernelGGL((combine_bwd_kernel<U, true, 3>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
+                               dots, T, k, rs, status);
+        else if (part == 3)
+            hipLaunchKernelGGL((combine_bwd_kernel<U, false, 3>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
+                               dots, T, k, rs, status);
+        else if (part == 1 && full)
+            hipLaunchKernelGGL((combine_bwd_kernel<U, true, 1>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
+                               dots, T, k, rs, status);
+        else if (part == 1)
+            hipLaunchKernelGGL((combine_bwd_kernel<U, false, 1>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
+                               dots, T, k, rs, status);
+        else if (full)
+            hipLaunchKernelGGL((combine_bwd_kernel<U, true, 2>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
+                               dots, T, k, rs, status);
+        else
+            hipLaunchKernelGGL((combine_bwd_kernel<U, false, 2>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
+                               dots, T, k, rs, status);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int64_t n = (int64_t)T * k;
     hipLaunchKernelGGL(gate_grad_kernel, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, dots, T, k,
                        rs.cpr, grad_w, status);
@@ -1244,7 +1285,8 @@ hipError_t launch_combine_backward(const void* grad_out, const void* ye, const f
                                    const int32_t* status, hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
-    return launch_combine_bwd_u<1>(grad_out, ye, w, comb_row, grad_ye, grad_w, dots, T, k, H / 8, status, s);
+    return launch_combine_bwd_u<MS_CBWD_UNIT>(grad_out, ye, w, comb_row, grad_ye, grad_w, dots, T, k, H / 8, status,
+                                              s);
 }
 
 }  // namespace ms

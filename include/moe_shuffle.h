@@ -237,8 +237,9 @@ int moe_shuffle_combine_rank_partial(moe_shuffle_plan_t plan, const void* ye, co
 /* Backward of combine, out[t] = sum_j w[t][j] * ye[comb_row[t][j]]:
  *   grad_ye[comb_row[t][j]] = bf16( fp32(w[t][j] * grad_out[t]) )
  *   grad_w[t][j] = sum over h of grad_out[t][h] * ye[comb_row[t][j]][h] in fp32:
- *     each lane sums its elements in ascending h, a butterfly adds the 64
- *     lanes, then the 512-element chunks of the row are added in order.
+ *     each lane sums its elements in ascending h, a fixed 6-level tree adds
+ *     the 64 lanes, then the chunks of the row (512 or 1024 elements) are
+ *     added in order.
  *   grad_out [T, H], ye [T*k, H], grad_ye [T*k, H] bf16; topk_w, grad_w fp32
  *   [T, k].  grad_ye must not overlap ye or grad_out.  Uses the plan
  *   workspace for the per-chunk partial sums. */

@@ -514,7 +514,11 @@ __device__ __forceinline__ void block_rows(int u0, int64_t n, const RowSplit& rs
 
 // Body shared by the send and fan-out kernels (two names, so that traces and
 // counters tell the two halves of dispatch apart).  WPB waves per block.
-template <int U, bool FULL, bool NTL, bool NTS, int WPB>
+// With the row count on the device and L > 1, each block takes L rounds of
+// WPB units, round i at unit block i * gridDim.x + blockIdx.x, so the grid
+// sized by the bound has L times fewer blocks and the rounds past the true
+// count end the block at once.
+template <int U, bool FULL, bool NTL, bool NTS, int WPB, int L>
 __device__ __forceinline__ void fanout_rows(int* s_tile, const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                             const int32_t* __restrict__ map, int width, int64_t n_bound,
                                             const int32_t* __restrict__ n_dev, RowSplit rs,
@@ -522,44 +526,51 @@ __device__ __forceinline__ void fanout_rows(int* s_tile, const u32x4* __restrict
 {
     if (status[0] != MOE_SHUFFLE_OK) return;
     const int64_t n = n_dev ? (int64_t)n_dev[0] : n_bound;
-    const int u0 = block_first_unit<WPB>(n_dev != nullptr);
-    int first, count;
-    block_rows<WPB>(u0, n, rs, &first, &count);
-    if (count <= 0) return;  // the whole block is past the last row
-    for (int i = threadIdx.x; i < count * width; i += WPB * kWave) s_tile[i] = map[(int64_t)first * width + i];
-    __syncthreads();
-
     const int wave = wave_id(), lane = lane_id();
-    const int u = u0 + wave;
-    const int row = fdiv(u, rs.div);
-    if (row >= n) return;
     const int V = rs.V;
-    const int c0 = (u - row * rs.cpr) * (kWave * U);
-    const u32x4* s = src + (int64_t)row * V + c0;
-    u32x4 v[U];
+#pragma unroll 1
+    for (int round = 0; round < L; ++round) {
+        const int u0 = L == 1 ? block_first_unit<WPB>(n_dev != nullptr)
+                              : (round * (int)gridDim.x + (int)blockIdx.x) * WPB;
+        if (L > 1 && (int64_t)u0 >= n * rs.cpr) return;  // uniform: every later round is empty too
+        int first, count;
+        block_rows<WPB>(u0, n, rs, &first, &count);
+        if (count <= 0) return;  // the whole block is past the last row
+        if (round > 0) __syncthreads();  // the previous round's targets are no longer read
+        for (int i = threadIdx.x; i < count * width; i += WPB * kWave) s_tile[i] = map[(int64_t)first * width + i];
+        __syncthreads();
+
+        const int u = u0 + wave;
+        const int row = fdiv(u, rs.div);
+        if (row < n) {
+            const int c0 = (u - row * rs.cpr) * (kWave * U);
+            const u32x4* s = src + (int64_t)row * V + c0;
+            u32x4 v[U];
 #pragma unroll
-    for (int i = 0; i < U; ++i)
-        if (FULL || c0 + i * kWave + lane < V) v[i] = load_row16<NTL>(s + i * kWave + lane);
-    const int* targets = s_tile + (row - first) * width;
-    for (int d = 0; d < width; ++d) {
-        const int p = __builtin_amdgcn_readfirstlane(targets[d]);
-        if (p < 0) break;
-        u32x4* o = dst + (int64_t)p * V + c0;
+            for (int i = 0; i < U; ++i)
+                if (FULL || c0 + i * kWave + lane < V) v[i] = load_row16<NTL>(s + i * kWave + lane);
+            const int* targets = s_tile + (row - first) * width;
+            for (int d = 0; d < width; ++d) {
+                const int p = __builtin_amdgcn_readfirstlane(targets[d]);
+                if (p < 0) break;
+                u32x4* o = dst + (int64_t)p * V + c0;
 #pragma unroll
-        for (int i = 0; i < U; ++i)
-            if (FULL || c0 + i * kWave + lane < V) store_row16<NTS>(v[i], o + i * kWave + lane);
+                for (int i = 0; i < U; ++i)
+                    if (FULL || c0 + i * kWave + lane < V) store_row16<NTS>(v[i], o + i * kWave + lane);
+            }
+        }
     }
 }
 
 #define MS_FANOUT_KERNEL(NAME, NTL, NTS)                                                                        \
-    template <int U, bool FULL, int WPB>                                                                         \
+    template <int U, bool FULL, int WPB, int L>                                                                  \
     __global__ __launch_bounds__(WPB * kWave) void NAME(const u32x4* __restrict__ src, u32x4* __restrict__ dst,  \
                                                         const int32_t* __restrict__ map, int width,             \
                                                         int64_t n_bound, const int32_t* __restrict__ n_dev,     \
                                                         RowSplit rs, const int32_t* __restrict__ status)        \
     {                                                                                                            \
         extern __shared__ int s_tile[]; /* [rows of this block][width] */                                        \
-        fanout_rows<U, FULL, NTL, NTS, WPB>(s_tile, src, dst, map, width, n_bound, n_dev, rs, status);           \
+        fanout_rows<U, FULL, NTL, NTS, WPB, L>(s_tile, src, dst, map, width, n_bound, n_dev, rs, status);        \
     }
 // x -> xr: source rows are tokens, targets their rank rows.
 MS_FANOUT_KERNEL(dispatch_send_kernel, MS_SEND_NT_LOAD, MS_SEND_NT_STORE)
@@ -602,30 +613,49 @@ static size_t tile_lds_bytes(int width, int arrays, int wpb)
     return sizeof(int) * (size_t)arrays * wpb * width;  // at most one row per wave
 }
 
-template <int U, int WPB>
-static hipError_t launch_fanout_uw(bool send, const void* src, void* dst, const int32_t* map, int width,
-                                   int64_t n_bound, const int32_t* n_dev, int V, const int32_t* status, hipStream_t s)
+// Rounds per block of the fan-out when the row count is on the device.
+// Measured on the MI355X (fan-out, grid sized by T*min(k,R)): two rounds
+// 302 -> 294 us (DeepSeek-V3-like) and 515 -> 470 us (skewed, where the
+// bound is twice the true count); four and eight rounds were slower.
+#ifndef MS_FANOUT_ROUNDS
+#define MS_FANOUT_ROUNDS 2
+#endif
+
+template <int U, int WPB, int L>
+static hipError_t launch_fanout_uwl(bool send, const void* src, void* dst, const int32_t* map, int width,
+                                    int64_t n_bound, const int32_t* n_dev, int V, const int32_t* status,
+                                    hipStream_t s)
 {
     RowSplit rs;
     if (!make_split(V, U, n_bound, &rs)) return hipErrorInvalidValue;
-    const dim3 grid(grid_for(n_bound * rs.cpr, WPB)), block(WPB * kWave);
+    const int64_t ublocks = (n_bound * rs.cpr + WPB - 1) / WPB;
+    const dim3 grid((unsigned)((ublocks + L - 1) / L)), block(WPB * kWave);
     const size_t lds = tile_lds_bytes(width, 1, WPB);
     const u32x4* sp = (const u32x4*)src;
     u32x4* dp = (u32x4*)dst;
     const bool full = V % (kWave * U) == 0;
     if (send && full)
-        hipLaunchKernelGGL((dispatch_send_kernel<U, true, WPB>), grid, block, lds, s, sp, dp, map, width, n_bound,
+        hipLaunchKernelGGL((dispatch_send_kernel<U, true, WPB, L>), grid, block, lds, s, sp, dp, map, width, n_bound,
                            n_dev, rs, status);
     else if (send)
-        hipLaunchKernelGGL((dispatch_send_kernel<U, false, WPB>), grid, block, lds, s, sp, dp, map, width, n_bound,
-                           n_dev, rs, status);
+        hipLaunchKernelGGL((dispatch_send_kernel<U, false, WPB, L>), grid, block, lds, s, sp, dp, map, width,
+                           n_bound, n_dev, rs, status);
     else if (full)
-        hipLaunchKernelGGL((dispatch_fanout_kernel<U, true, WPB>), grid, block, lds, s, sp, dp, map, width, n_bound,
-                           n_dev, rs, status);
+        hipLaunchKernelGGL((dispatch_fanout_kernel<U, true, WPB, L>), grid, block, lds, s, sp, dp, map, width,
+                           n_bound, n_dev, rs, status);
     else
-        hipLaunchKernelGGL((dispatch_fanout_kernel<U, false, WPB>), grid, block, lds, s, sp, dp, map, width,
+        hipLaunchKernelGGL((dispatch_fanout_kernel<U, false, WPB, L>), grid, block, lds, s, sp, dp, map, width,
                            n_bound, n_dev, rs, status);
     return hipGetLastError();
+}
+
+template <int U, int WPB>
+static hipError_t launch_fanout_uw(bool send, const void* src, void* dst, const int32_t* map, int width,
+                                   int64_t n_bound, const int32_t* n_dev, int V, const int32_t* status, hipStream_t s)
+{
+    if (n_dev && MS_FANOUT_ROUNDS > 1)
+        return launch_fanout_uwl<U, WPB, MS_FANOUT_ROUNDS>(send, src, dst, map, width, n_bound, n_dev, V, status, s);
+    return launch_fanout_uwl<U, WPB, 1>(send, src, dst, map, width, n_bound, n_dev, V, status, s);
 }
 
 template <int U>
@@ -668,7 +698,7 @@ hipError_t launch_fanout_rows(bool send, const void* src, void* dst, const int32
 // range are, in each rank segment r, the contiguous rows
 //   [rank_offset[r] + P_r(t0), rank_offset[r] + P_r(t1)),
 // P_r(t) = tokens before t that reach rank r, read from the plan's tile
-// bases (t a multiple of the 256-token plan tile) or, at t = T, the rank's
+// bases (t a multiple of the 64-token plan tile) or, at t = T, the rank's
 // count.  Each block rebuilds that table for itself (no shared scratch, so
 // ranges on different streams never race) and each wave finds its segment
 // by binary search.
@@ -824,36 +854,12 @@ __device__ __forceinline__ float reduce_scatter8(const float p[8], int lane)
 
 enum WeightMode { kUnweighted = 0, kPerSlot = 1, kPerSourceRow = 2 };
 
-template <int U, bool FULL, int WMODE, bool NTL, bool NTS, int WPB, int MAXW>
-__device__ __forceinline__ void reduce_rows(int* s_tile, const u32x4* __restrict__ src,
-                                            const int32_t* __restrict__ map, int width,
-                                            const float* __restrict__ w, u32x4* __restrict__ out, int64_t n_bound,
-                                            const int32_t* __restrict__ n_dev, RowSplit rs,
-                                            const int32_t* __restrict__ status)
+// One wave's unit: chunk c0 of output row `row`, its map row and gates in LDS.
+template <int U, bool FULL, int WMODE, bool NTL, bool NTS, int MAXW>
+__device__ __forceinline__ void reduce_unit_row(const u32x4* __restrict__ src, const int* trow, const int* tw,
+                                                int width, const float* __restrict__ w, u32x4* __restrict__ out,
+                                                int row, int c0, int V, int lane)
 {
-    if (status[0] != MOE_SHUFFLE_OK) return;
-    const int64_t n = n_dev ? (int64_t)n_dev[0] : n_bound;
-    const int u0 = block_first_unit<WPB>(n_dev != nullptr);
-    int first, count;
-    block_rows<WPB>(u0, n, rs, &first, &count);
-    if (count <= 0) return;
-    int* s_rows = s_tile;                               // [rows of this block][width]
-    int* s_w = s_tile + WPB * width;                    // per-slot gates, same shape
-    for (int i = threadIdx.x; i < count * width; i += WPB * kWave) {
-        s_rows[i] = map[(int64_t)first * width + i];
-        if (WMODE == kPerSlot) s_w[i] = __float_as_int(w[(int64_t)first * width + i]);
-    }
-    __syncthreads();
-
-    const int wave = wave_id(), lane = lane_id();
-    const int u = u0 + wave;
-    const int row = fdiv(u, rs.div);
-    if (row >= n) return;
-    const int V = rs.V;
-    const int c0 = (u - row * rs.cpr) * (kWave * U);
-    const int* trow = s_rows + (row - first) * width;
-    const int* tw = s_w + (row - first) * width;
-
     float acc[U][8];
 #pragma unroll
     for (int i = 0; i < U; ++i)
@@ -946,8 +952,46 @@ __device__ __forceinline__ void reduce_rows(int* s_tile, const u32x4* __restrict
     }
 }
 
+// Stages the map rows (and per-slot gates) of the block's units in LDS, then
+// one unit per wave.  With the row count on the device and L > 1, each
+// block takes L rounds of WPB units (as fanout_rows does).
+template <int U, bool FULL, int WMODE, bool NTL, bool NTS, int WPB, int MAXW, int L>
+__device__ __forceinline__ void reduce_rows(int* s_tile, const u32x4* __restrict__ src,
+                                            const int32_t* __restrict__ map, int width,
+                                            const float* __restrict__ w, u32x4* __restrict__ out, int64_t n_bound,
+                                            const int32_t* __restrict__ n_dev, RowSplit rs,
+                                            const int32_t* __restrict__ status)
+{
+    if (status[0] != MOE_SHUFFLE_OK) return;
+    const int64_t n = n_dev ? (int64_t)n_dev[0] : n_bound;
+    const int wave = wave_id(), lane = lane_id();
+    int* s_rows = s_tile;             // [rows of this block][width]
+    int* s_w = s_tile + WPB * width;  // per-slot gates, same shape
+#pragma unroll 1
+    for (int round = 0; round < L; ++round) {
+        const int u0 = L == 1 ? block_first_unit<WPB>(n_dev != nullptr)
+                              : (round * (int)gridDim.x + (int)blockIdx.x) * WPB;
+        if (L > 1 && (int64_t)u0 >= n * rs.cpr) return;  // uniform: every later round is empty too
+        int first, count;
+        block_rows<WPB>(u0, n, rs, &first, &count);
+        if (count <= 0) return;
+        if (round > 0) __syncthreads();  // the previous round's map rows are no longer read
+        for (int i = threadIdx.x; i < count * width; i += WPB * kWave) {
+            s_rows[i] = map[(int64_t)first * width + i];
+            if (WMODE == kPerSlot) s_w[i] = __float_as_int(w[(int64_t)first * width + i]);
+        }
+        __syncthreads();
+        const int u = u0 + wave;
+        const int row = fdiv(u, rs.div);
+        if (row < n)
+            reduce_unit_row<U, FULL, WMODE, NTL, NTS, MAXW>(src, s_rows + (row - first) * width,
+                                                            s_w + (row - first) * width, width, w, out, row,
+                                                            (u - row * rs.cpr) * (kWave * U), rs.V, lane);
+    }
+}
+
 #define MS_REDUCE_KERNEL(NAME, NTL, NTS)                                                                         \
-    template <int U, bool FULL, int WMODE, int WPB, int MAXW>                                                    \
+    template <int U, bool FULL, int WMODE, int WPB, int MAXW, int L>                                             \
     __global__ __launch_bounds__(WPB * kWave) void NAME(const u32x4* __restrict__ src,                           \
                                                         const int32_t* __restrict__ map, int width,             \
                                                         const float* __restrict__ w, u32x4* __restrict__ out,   \
@@ -955,8 +999,8 @@ __device__ __forceinline__ void reduce_rows(int* s_tile, const u32x4* __restrict
                                                         RowSplit rs, const int32_t* __restrict__ status)        \
     {                                                                                                            \
         extern __shared__ int s_tile[];                                                                          \
-        reduce_rows<U, FULL, WMODE, NTL, NTS, WPB, MAXW>(s_tile, src, map, width, w, out, n_bound, n_dev, rs,    \
-                                                         status);                                                \
+        reduce_rows<U, FULL, WMODE, NTL, NTS, WPB, MAXW, L>(s_tile, src, map, width, w, out, n_bound, n_dev, rs, \
+                                                            status);                                             \
     }
 // ye (expert-major) -> out (token-major): the forward combine.
 MS_REDUCE_KERNEL(combine_rows_kernel, MS_COMBINE_NT_LOAD, MS_COMBINE_NT_STORE)
@@ -993,20 +1037,33 @@ static int reduce_unit(int kind, int V, int64_t src_bytes)
 
 enum ReduceKind { kCombine = 0, kSumExpertRows = 1, kSumRankRows = 2 };
 
-template <int KIND, int U, bool FULL, int WMODE, int WPB, int MAXW>
+// Rounds per block of the receiver's sum: two rounds measured slower there
+// (280 -> 297 us, DeepSeek-V3-like), so one.
+#ifndef MS_SUMX_ROUNDS
+#define MS_SUMX_ROUNDS 1
+#endif
+
+template <int KIND, int U, bool FULL, int WMODE, int WPB, int MAXW, int L>
 static void launch_reduce_kernel(dim3 grid, size_t lds, hipStream_t s, const u32x4* src, const int32_t* map,
                                  int width, const float* w, u32x4* out, int64_t n_bound, const int32_t* n_dev,
                                  RowSplit rs, const int32_t* status)
 {
     const dim3 block(WPB * kWave);
     if constexpr (KIND == kCombine)
-        hipLaunchKernelGGL((combine_rows_kernel<U, FULL, WMODE, WPB, MAXW>), grid, block, lds, s, src, map, width, w,
-                           out, n_bound, n_dev, rs, status);
-    else if constexpr (KIND == kSumExpertRows)
-        hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW>), grid, block, lds, s, src, map, width,
+        hipLaunchKernelGGL((combine_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1>), grid, block, lds, s, src, map, width,
                            w, out, n_bound, n_dev, rs, status);
+    else if constexpr (KIND == kSumExpertRows && L > 1) {
+        if (n_dev)
+            hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW, L>), grid, block, lds, s, src, map,
+                               width, w, out, n_bound, n_dev, rs, status);
+        else
+            hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1>), grid, block, lds, s, src, map,
+                               width, w, out, n_bound, n_dev, rs, status);
+    } else if constexpr (KIND == kSumExpertRows)
+        hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1>), grid, block, lds, s, src, map,
+                           width, w, out, n_bound, n_dev, rs, status);
     else
-        hipLaunchKernelGGL((sum_rank_rows_kernel<U, FULL, WMODE, WPB, MAXW>), grid, block, lds, s, src, map, width,
+        hipLaunchKernelGGL((sum_rank_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1>), grid, block, lds, s, src, map, width,
                            w, out, n_bound, n_dev, rs, status);
 }
 
@@ -1016,22 +1073,26 @@ static hipError_t launch_reduce_uw(const void* src, const int32_t* map, int widt
 {
     RowSplit rs;
     if (!make_split(V, U, n_bound, &rs)) return hipErrorInvalidValue;
-    const dim3 grid(grid_for(n_bound * rs.cpr, WPB));
+    // rounds only where the row count is on the device (the receiver's sum)
+    constexpr int L = KIND == kSumExpertRows ? MS_SUMX_ROUNDS : 1;
+    const int64_t ublocks = (n_bound * rs.cpr + WPB - 1) / WPB;
+    const int rounds = n_dev ? L : 1;
+    const dim3 grid((unsigned)((ublocks + rounds - 1) / rounds));
     const size_t lds = tile_lds_bytes(width, 2, WPB);
     const u32x4* sp = (const u32x4*)src;
     u32x4* op = (u32x4*)out;
     const bool full = V % (kWave * U) == 0;
     if (width <= 8 && full)
-        launch_reduce_kernel<KIND, U, true, WMODE, WPB, 8>(grid, lds, s, sp, map, width, w, op, n_bound, n_dev, rs,
+        launch_reduce_kernel<KIND, U, true, WMODE, WPB, 8, L>(grid, lds, s, sp, map, width, w, op, n_bound, n_dev, rs,
                                                            status);
     else if (width <= 8)
-        launch_reduce_kernel<KIND, U, false, WMODE, WPB, 8>(grid, lds, s, sp, map, width, w, op, n_bound, n_dev, rs,
+        launch_reduce_kernel<KIND, U, false, WMODE, WPB, 8, L>(grid, lds, s, sp, map, width, w, op, n_bound, n_dev, rs,
                                                             status);
     else if (full)
-        launch_reduce_kernel<KIND, U, true, WMODE, WPB, kMaxTopK>(grid, lds, s, sp, map, width, w, op, n_bound,
+        launch_reduce_kernel<KIND, U, true, WMODE, WPB, kMaxTopK, L>(grid, lds, s, sp, map, width, w, op, n_bound,
                                                                   n_dev, rs, status);
     else
-        launch_reduce_kernel<KIND, U, false, WMODE, WPB, kMaxTopK>(grid, lds, s, sp, map, width, w, op, n_bound,
+        launch_reduce_kernel<KIND, U, false, WMODE, WPB, kMaxTopK, L>(grid, lds, s, sp, map, width, w, op, n_bound,
                                                                    n_dev, rs, status);
     return hipGetLastError();
 }
@@ -1108,23 +1169,22 @@ hipError_t launch_sum_rank_rows(const void* src, int64_t src_rows, const int32_t
 //   grad_w[t][j]    = sum_h grad_out[t][h] * ye[q(t,j)][h]
 // One wave per 64*U-vector chunk of a token's row: the chunk of grad_out is
 // loaded once and reused for all k slots.  The gate gradient is summed in a
-// fixed order: each lane over its elements (ascending h), a butterfly over
-// the 64 lanes (one 6-level tree per slot), then (second kernel) the chunks
-// of a row in ascending order.
-// Each bf16 x bf16 product is exact in fp32.
+// fixed order: each lane over its 8U elements (ascending h), a 6-level tree
+// over the 64 lanes, then (gate_grad_kernel) the chunks of a row in
+// ascending order.  Each bf16 x bf16 product is exact in fp32.
 
-// PART selects the work: 1 = grad_ye rows only, 2 = gate-gradient partials
-// only, 3 = both in one pass.
+// PART selects the work: 1 = the grad_ye rows, 2 = the gate-gradient
+// partials.  Two passes: a write-heavy one (read grad_out, write k rows)
+// and a read-only one (read grad_out and k rows) ran 366 us against 423 us
+// for one pass doing both (DeepSeek-V3-like workload, MI355X), whose mix
+// of k row reads and k row writes per token kept HBM from streaming.
 template <int U, bool FULL, int PART>
-__global__ __launch_bounds__(kBlock) void combine_bwd_kernel(const u32x4* __restrict__ grad_out,
-                                                             const u32x4* __restrict__ ye,
-                                                             const float* __restrict__ w,
-                                                             const int32_t* __restrict__ comb_row,
-                                                             u32x4* __restrict__ grad_ye, float* __restrict__ dots,
-                                                             int T, int k, RowSplit rs,
-                                                             const int32_t* __restrict__ status)
+__device__ __forceinline__ void combine_bwd_rows(int* s_tile, const u32x4* __restrict__ grad_out,
+                                                 const u32x4* __restrict__ ye, const float* __restrict__ w,
+                                                 const int32_t* __restrict__ comb_row, u32x4* __restrict__ grad_ye,
+                                                 float* __restrict__ dots, int T, int k, RowSplit rs,
+                                                 const int32_t* __restrict__ status)
 {
-    extern __shared__ int s_tile[];
     if (status[0] != MOE_SHUFFLE_OK) return;
     int first, count;
     block_rows<kWavesPerBlock>((int)blockIdx.x * kWavesPerBlock, T, rs, &first, &count);
@@ -1214,6 +1274,23 @@ __global__ __launch_bounds__(kBlock) void combine_bwd_kernel(const u32x4* __rest
     }
 }
 
+#define MS_CBWD_KERNEL(NAME, PART)                                                                               \
+    template <int U, bool FULL>                                                                                   \
+    __global__ __launch_bounds__(kBlock) void NAME(const u32x4* __restrict__ grad_out,                            \
+                                                   const u32x4* __restrict__ ye, const float* __restrict__ w,     \
+                                                   const int32_t* __restrict__ comb_row,                          \
+                                                   u32x4* __restrict__ grad_ye, float* __restrict__ dots, int T,  \
+                                                   int k, RowSplit rs, const int32_t* __restrict__ status)        \
+    {                                                                                                             \
+        extern __shared__ int s_tile[];                                                                           \
+        combine_bwd_rows<U, FULL, PART>(s_tile, grad_out, ye, w, comb_row, grad_ye, dots, T, k, rs, status);      \
+    }
+// grad_ye[comb_row[t][j]] = bf16(w[t][j] * grad_out[t]).
+MS_CBWD_KERNEL(combine_bwd_grad_kernel, 1)
+// dots[t][chunk][j] = the chunk's share of <grad_out[t], ye[comb_row[t][j]]>.
+MS_CBWD_KERNEL(combine_bwd_dot_kernel, 2)
+#undef MS_CBWD_KERNEL
+
 // grad_w[t][j] = sum over chunks c (ascending) of dots[t][c][j].
 __global__ __launch_bounds__(kBlock) void gate_grad_kernel(const float* __restrict__ dots, int T, int k, int cpr,
                                                            float* __restrict__ grad_w,
@@ -1229,55 +1306,58 @@ __global__ __launch_bounds__(kBlock) void gate_grad_kernel(const float* __restri
     grad_w[i] = acc;
 }
 
-#ifndef MS_CBWD_SPLIT
-#define MS_CBWD_SPLIT 0
+// Vectors per lane of a unit in the two passes (measured on the MI355X,
+// DeepSeek-V3-like workload: grad_ye 182 us at U = 1 against 218 us at
+// U = 2; the partials 180 us at U = 2 against 243 us at U = 1).
+#ifndef MS_CBWD_GRAD_UNIT
+#define MS_CBWD_GRAD_UNIT 1
 #endif
-#ifndef MS_CBWD_UNIT
-#define MS_CBWD_UNIT 1
+#ifndef MS_CBWD_DOT_UNIT
+#define MS_CBWD_DOT_UNIT 2
+#endif
+#ifndef MS_CBWD_DOT_FIRST
+#define MS_CBWD_DOT_FIRST 0
 #endif
 
 template <int U>
-static hipError_t launch_combine_bwd_u(const void* grad_out, const void* ye, const float* w, const int32_t* comb_row,
-                                       void* grad_ye, float* grad_w, float* dots, int T, int k, int V,
-                                       const int32_t* status, hipStream_t s)
+static hipError_t launch_cbwd_pass(bool grad, const void* grad_out, const void* ye, const float* w,
+                                   const int32_t* comb_row, void* grad_ye, float* dots, int T, int k, int V,
+                                   const int32_t* status, hipStream_t s, int* cpr)
 {
     RowSplit rs;
     if (!make_split(V, U, T, &rs)) return hipErrorInvalidValue;
+    *cpr = rs.cpr;
     const dim3 grid(grid_for((int64_t)T * rs.cpr, kWavesPerBlock));
     const size_t lds = tile_lds_bytes(k, 2, kWavesPerBlock);
     const u32x4* gp = (const u32x4*)grad_out;
     const u32x4* yp = (const u32x4*)ye;
     u32x4* gyp = (u32x4*)grad_ye;
-    constexpr int parts[2][2] = {{3, 0}, {1, 2}};
-    for (int pass = 0; pass < 2; ++pass) {
-        const int part = parts[MS_CBWD_SPLIT][pass];
-        if (part == 0) break;
-        const bool full = V % (kWave * U) == 0;
-        if (part == 3 && full)
-            hipLaunchKernelGGL((combine_bwd_kernel<U, true, 3>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
-                               dots, T, k, rs, status);
-        else if (part == 3)
-            hipLaunchKernelGGL((combine_bwd_kernel<U, false, 3>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
-                               dots, T, k, rs, status);
-        else if (part == 1 && full)
-            hipLaunchKernelGGL((combine_bwd_kernel<U, true, 1>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
-                               dots, T, k, rs, status);
-        else if (part == 1)
-            hipLaunchKernelGGL((combine_bwd_kernel<U, false, 1>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
-                               dots, T, k, rs, status);
-        else if (full)
-            hipLaunchKernelGGL((combine_bwd_kernel<U, true, 2>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
-                               dots, T, k, rs, status);
-        else
-            hipLaunchKernelGGL((combine_bwd_kernel<U, false, 2>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
-                               dots, T, k, rs, status);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    const int64_t n = (int64_t)T * k;
-    hipLaunchKernelGGL(gate_grad_kernel, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, dots, T, k,
-                       rs.cpr, grad_w, status);
+    const bool full = V % (kWave * U) == 0;
+    if (grad && full)
+        hipLaunchKernelGGL((combine_bwd_grad_kernel<U, true>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
+                           dots, T, k, rs, status);
+    else if (grad)
+        hipLaunchKernelGGL((combine_bwd_grad_kernel<U, false>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
+                           dots, T, k, rs, status);
+    else if (full)
+        hipLaunchKernelGGL((combine_bwd_dot_kernel<U, true>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
+                           dots, T, k, rs, status);
+    else
+        hipLaunchKernelGGL((combine_bwd_dot_kernel<U, false>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
+                           dots, T, k, rs, status);
     return hipGetLastError();
+}
+
+static hipError_t launch_cbwd(bool grad, int U, const void* grad_out, const void* ye, const float* w,
+                              const int32_t* comb_row, void* grad_ye, float* dots, int T, int k, int V,
+                              const int32_t* status, hipStream_t s, int* cpr)
+{
+    switch (U) {
+        case 1: return launch_cbwd_pass<1>(grad, grad_out, ye, w, comb_row, grad_ye, dots, T, k, V, status, s, cpr);
+        case 2: return launch_cbwd_pass<2>(grad, grad_out, ye, w, comb_row, grad_ye, dots, T, k, V, status, s, cpr);
+        case 4: return launch_cbwd_pass<4>(grad, grad_out, ye, w, comb_row, grad_ye, dots, T, k, V, status, s, cpr);
+        default: return launch_cbwd_pass<8>(grad, grad_out, ye, w, comb_row, grad_ye, dots, T, k, V, status, s, cpr);
+    }
 }
 
 hipError_t launch_combine_backward(const void* grad_out, const void* ye, const float* w, const int32_t* comb_row,
@@ -1285,8 +1365,18 @@ hipError_t launch_combine_backward(const void* grad_out, const void* ye, const f
                                    const int32_t* status, hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
-    return launch_combine_bwd_u<MS_CBWD_UNIT>(grad_out, ye, w, comb_row, grad_ye, grad_w, dots, T, k, H / 8, status,
-                                              s);
+    const int V = H / 8;
+    int cpr = 0, unused = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool grad = (pass == 0) != (MS_CBWD_DOT_FIRST != 0);
+        const hipError_t e = launch_cbwd(grad, fit_unit(V, grad ? MS_CBWD_GRAD_UNIT : MS_CBWD_DOT_UNIT), grad_out, ye,
+                                         w, comb_row, grad_ye, dots, T, k, V, status, s, grad ? &unused : &cpr);
+        if (e != hipSuccess) return e;
+    }
+    const int64_t n = (int64_t)T * k;
+    hipLaunchKernelGGL(gate_grad_kernel, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, dots, T, k,
+                       cpr, grad_w, status);
+    return hipGetLastError();
 }
 
 }  // namespace ms

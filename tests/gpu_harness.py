@@ -153,8 +153,10 @@ def check_backward_case(idx, w, H, E, R, ye, grad_xe, grad_out, name=""):
     np.testing.assert_array_equal(to_host16(gye)[:T * k], o_gye, err_msg="grad_ye")
     if T:
         got = gw.cpu().numpy()[:T * k].reshape(T, k).astype(np.float64)
-        cpr = -(-(H // 8) // 64)
-        bound = (8 + 6 + cpr + 2) * 2.0 ** -24 * abs_dot(o["comb_row"], grad_out, ye) + 2.0 ** -126
+        # per lane 8U products in order, a 6-level tree over the lanes, then the
+        # row's chunks of 512U elements in order: U = 1 or 2 (the library's unit)
+        terms = max(8 * u + 6 + -(-(H // 8) // (64 * u)) + 2 for u in (1, 2))
+        bound = terms * 2.0 ** -24 * abs_dot(o["comb_row"], grad_out, ye) + 2.0 ** -126
         err = np.abs(got - o_gw)
         say(f"[bwd] {name} N={N} grad_w max err / bound {float((err / bound).max()):.3g}")
         assert np.all(err <= bound)

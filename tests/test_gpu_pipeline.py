@@ -74,6 +74,8 @@ def test_pipelined_ranges_match_oracle(cfg_id, chunks):
     (700, 7168, 256, 8, 32, [0, 512, 700]),
     (513, 264, 24, 24, 6, [0, 256, 512, 513]),
     (300, 96, 12, 3, 1, [0, 300]),
+    (1000, 1032, 32, 4, 8, [0, 64, 192, 640, 1000]),   # ranges on the 64-token plan tile
+    (130, 64, 16, 4, 4, [0, 64, 128, 130]),
 ])
 def test_ragged_ranges(T, H, E, k, R, bounds):
     import gpu_harness as h
@@ -104,7 +106,7 @@ def test_range_arguments():
     xe = torch.zeros((T * k, H), dtype=torch.int16, device="cuda")
     out = torch.zeros((T, H), dtype=torch.int16, device="cuda")
     w_d = torch.from_numpy(w).cuda()
-    for t0, t1 in [(100, 256), (0, 300), (256, 128), (0, 601), (-256, 0)]:
+    for t0, t1 in [(100, 256), (0, 300), (256, 128), (0, 601), (-256, 0), (32, 64), (0, 96)]:
         with pytest.raises(ms.MoeShuffleError) as e:
             ms.moe_shuffle_dispatch_range(plan, x, xr, xe, t0, t1)
         assert e.value.code == ms.E_INVALID_ARG

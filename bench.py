@@ -50,6 +50,17 @@ def bf16_order(u):
     return np.where(u & 0x8000, 0x8000 - (u & 0x7FFF), 0x8000 + u)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def source_digest() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
@@ -490,6 +501,7 @@ def main():
     names = ("plan", "send", "fanout", "combine")
     us = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]) * 1e3)
           for j, n in enumerate(names)}
+    step_ms = np.array([events[i][0].elapsed_time(events[i][4]) for i in range(args.steps)])
     info = ms.moe_shuffle_plan_query(last_plan)
     N = info["N"]
     B = algorithmic_bytes(T, H, k, N)
@@ -525,28 +537,37 @@ def main():
         xe_ok = np.array_equal(xe.cpu().numpy().view(np.uint16), oxe)
         oout = orc.combine(o["comb_row"], oxe, inp["topk_w"], E, R)
         got = out.cpu().numpy().view(np.uint16)
+        # the identity expert (ye = xe) with gates summing to 1 returns x, -0 as +0
+        x_rt = np.where(inp["x"] == 0x8000, 0, inp["x"]).astype(np.uint16)
         parity = {"plan_bitexact": bool(plan_ok), "xr_bitexact": bool(xr_ok), "xe_bitexact": bool(xe_ok),
                   "out_max_ulp": int(np.abs(bf16_order(got) - bf16_order(oout)).max()),
-                  "out_bitexact": bool(np.array_equal(got, oout))}
+                  "out_ndiff": int((got != oout).sum()), "out_bitexact": bool(np.array_equal(got, oout)),
+                  "roundtrip_bitexact": bool(np.array_equal(got, x_rt))}
         log(f"[bench] parity vs oracle: {parity}")
 
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         orc = oracle.get()
-        reps, tcpu = 0, 0.0
-        while reps == 0 or (tcpu < args.cpu_budget_s and reps < 20):
-            s0 = time.perf_counter()
-            rc, o = orc.plan(inp["topk_idx"], H, E, R)
-            oxr, oxe = orc.dispatch(o, inp["x"], E, k, R)
-            orc.combine(o["comb_row"], oxe, inp["topk_w"], E, R)
-            tcpu += time.perf_counter() - s0
-            reps += 1
+        allowed = sorted(os.sched_getaffinity(0))
+        os.sched_setaffinity(0, {allowed[0]})  # the oracle is single-threaded: pin it to one core
+        try:
+            reps, tcpu = 0, 0.0
+            while reps == 0 or (tcpu < args.cpu_budget_s and reps < 20):
+                s0 = time.perf_counter()
+                rc, o = orc.plan(inp["topk_idx"], H, E, R)
+                oxr, oxe = orc.dispatch(o, inp["x"], E, k, R)
+                orc.combine(o["comb_row"], oxe, inp["topk_w"], E, R)
+                tcpu += time.perf_counter() - s0
+                reps += 1
+        finally:
+            os.sched_setaffinity(0, set(allowed))
         t_rep = tcpu / reps
         cpu = {"value": round(B["total"] / t_rep / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"the full {cfg.name} workload, {reps} pass(es) of plan+dispatch+combine, "
-                         f"single-threaded C oracle, {t_rep:.2f} s per pass",
-               "tokens_per_s": round(T / t_rep, 1), "host_cpus": os.cpu_count()}
+                         f"single-threaded C oracle pinned to one core, {t_rep:.2f} s per pass",
+               "tokens_per_s": round(T / t_rep, 1), "host_cpus": os.cpu_count(),
+               "host_cpus_allowed": len(allowed), "cpu_model": cpu_model()}
         log(f"[bench] cpu oracle: {cpu}")
 
     # dominant kernel by algorithmic bytes: the receiver fan-out
@@ -566,6 +587,7 @@ def main():
         "dispatch_combine_GBps": round((B["send"] + B["fanout"] + B["combine"]) / (dc_us * 1e-6) / 1e9, 1),
         "dispatch_combine_frac_of_peak": round((B["total"]) / (dc_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
         "kernel_us": {n: round(us[n], 2) for n in names},
+        "step_ms_event_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
         "algorithmic_bytes": B,
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "accumulate": "fp32",

@@ -81,6 +81,22 @@ def test_all_tokens_one_expert_skew():
     harness().check_case(idx, x, w, H, E, R, name="one-hot-expert")
 
 
+def test_all_experts_on_one_rank():
+    """Every token sends to one rank only: N = T, an eighth of the host-side
+    bound T*min(k,R), so most blocks of the fan-out grid find no row."""
+    rng = np.random.default_rng(8)
+    T, H, E, k, R = 1000, 520, 64, 8, 8
+    epr = E // R
+    idx = np.empty((T, k), np.int32)
+    for t in range(T):
+        r = rng.integers(R)
+        idx[t] = r * epr + rng.permutation(epr)[:k]
+    w = rng.random((T, k)).astype(np.float32)
+    x = synth.random_bf16(rng, (T, H))
+    g, o = harness().check_case(idx, x, w, H, E, R, name="one-rank-per-token")
+    assert o["N"] == T
+
+
 def test_plan_without_query_uses_upper_bound():
     """Dispatch sized by T*min(k,R) without a host sync gives the same bits."""
     h = harness()

@@ -248,16 +248,20 @@ def bench_path(args):
     for _ in range(args.warmup):
         for c in calls:
             c()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(args.steps):   # the timed region: nothing between the calls
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    for i in range(args.steps):   # the per-call breakdown, with HIP events between the calls
         events[i][0].record()
         for j, c in enumerate(calls):
             c()
             events[i][j + 1].record()
     torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     us = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]) * 1e3)
           for j, n in enumerate(names)}
     B = path_bytes(args.path, T, H, k, N)
@@ -486,18 +490,29 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # The timed region: K steps with nothing between the calls (an event
+    # marker between two kernels costs a few microseconds of its own).
     plans = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        plans.append(step(events[i]))
+        plans.append(step())
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    for p in plans:
+        ms.moe_shuffle_plan_destroy(p)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # The per-kernel breakdown: K more steps with HIP events recorded between
+    # the calls on the stream they run on.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    plans = []
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        plans.append(step(events[i]))
+    torch.cuda.synchronize()
     last_plan = plans[-1]
     for p in plans[:-1]:
         ms.moe_shuffle_plan_destroy(p)
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
     names = ("plan", "send", "fanout", "combine")
     us = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]) * 1e3)
           for j, n in enumerate(names)}

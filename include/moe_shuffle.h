@@ -43,8 +43,8 @@
  *  - Every function returns an int status (MOE_SHUFFLE_OK or a negative
  *    code below); nothing is thrown across the ABI.  A failing call writes
  *    no output.
- *  - Implementation limits: E + R <= 1024, k <= 64, T * k < 2^31
- *    (otherwise MOE_SHUFFLE_E_OVERFLOW).
+ *  - Implementation limits: E + R <= 1024, k <= 64, T * k < 2^31 and
+ *    T * k * ceil(H / 512) < 2^31 - 64 (otherwise MOE_SHUFFLE_E_OVERFLOW).
  */
 #ifndef MOE_SHUFFLE_H
 #define MOE_SHUFFLE_H

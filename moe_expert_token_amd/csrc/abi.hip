@@ -37,6 +37,10 @@ int check_dims(const moe_shuffle_dims* d)
     if (d->hidden % 8 != 0) return MOE_SHUFFLE_E_ALIGN;
     if ((int64_t)d->num_tokens * d->top_k >= ((int64_t)1 << 31)) return MOE_SHUFFLE_E_OVERFLOW;
     if (d->top_k > ms::kMaxTopK || d->num_experts + d->num_ranks > ms::kMaxCols) return MOE_SHUFFLE_E_OVERFLOW;
+    // kernels index 512-element pieces of rows with int: every row count
+    // (at most T*k) times the pieces per row must stay below 2^31
+    const int64_t pieces = ((int64_t)d->hidden / 8 + ms::kWave - 1) / ms::kWave;
+    if ((int64_t)d->num_tokens * d->top_k * pieces + 64 >= ((int64_t)1 << 31)) return MOE_SHUFFLE_E_OVERFLOW;
     return MOE_SHUFFLE_OK;
 }
 

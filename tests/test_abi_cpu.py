@@ -52,11 +52,13 @@ def test_dims_codes_match_oracle(d):
 
 def test_implementation_limits():
     ms, lib = _lib()
-    for d in [(4, 8, 128, 65, 4), (4, 8, 1024, 2, 8)]:
+    # k > 64; E + R > 1024; T*k*ceil(H/512) past 2^31 - 64 with T*k < 2^31
+    for d in [(4, 8, 128, 65, 4), (4, 8, 1024, 2, 8), (1 << 25, 4096, 16, 8, 4), ((1 << 28) - 1, 520, 16, 8, 4)]:
         with pytest.raises(ms.MoeShuffleError) as e:
             ms.moe_shuffle_workspace_size(ms.dims_of(*d))
         assert e.value.code == ms.E_OVERFLOW
     assert ms.moe_shuffle_workspace_size(ms.dims_of(4, 8, 1024 - 64, 8, 64)) > 0
+    assert ms.moe_shuffle_workspace_size(ms.dims_of((1 << 25) - 16, 4096, 16, 8, 4)) > 0
 
 
 def test_plan_rejects_bad_pointers_before_any_launch():

@@ -214,6 +214,56 @@ struct PlaceArgs {
     int32_t *rank_segs, *expert_segs, *n_rank_rows;
 };
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Writes one lane's index row of `width` entries, -1 padded: with width a
+// multiple of 4, in 16-byte groups (the row start is 16-byte aligned);
+// otherwise one entry at a time.
+struct RowWriter {
+    int32_t* row;
+    int width, n;
+    bool vec;
+    i32x4 pend;
+
+    __device__ RowWriter(int32_t* r, int w) : row(r), width(w), n(0), vec((w & 3) == 0), pend{-1, -1, -1, -1} {}
+    __device__ void start(int32_t* r)
+    {
+        row = r;
+        n = 0;
+        pend = i32x4{-1, -1, -1, -1};
+    }
+    __device__ void put(int v)
+    {
+        if (vec) {
+            const int i = n & 3;
+            pend.x = i == 0 ? v : pend.x;
+            pend.y = i == 1 ? v : pend.y;
+            pend.z = i == 2 ? v : pend.z;
+            pend.w = i == 3 ? v : pend.w;
+            if (i == 3) {
+                *(i32x4*)(row + (n & ~3)) = pend;
+                pend = i32x4{-1, -1, -1, -1};
+            }
+        } else {
+            row[n] = v;
+        }
+        ++n;
+    }
+    __device__ void finish()
+    {
+        if (vec) {
+            int g = n & ~3;
+            if (n & 3) {
+                *(i32x4*)(row + g) = pend;
+                g += 4;
+            }
+            for (; g < width; g += 4) *(i32x4*)(row + g) = i32x4{-1, -1, -1, -1};
+        } else {
+            for (int i = n; i < width; ++i) row[i] = -1;
+        }
+    }
+};
+
 template <int KMAX>
 __global__ __launch_bounds__(kWave) void plan_place_kernel(PlaceArgs a)
 {
@@ -316,15 +366,22 @@ __global__ __launch_bounds__(kWave) void plan_place_kernel(PlaceArgs a)
     const int* wb = s_wbase;
     const int KR = a.KR, D = a.D;
 
-    // Expert row of every slot, in slot order.
+    // Expert row of every slot, in slot order.  Index rows whose width is a
+    // multiple of 4 go out as 16-byte stores (a lane's row is contiguous).
     int qv[KMAX];
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-        qv[j] = 0;
-        if (j < k) {
-            qv[j] = wb[ev[j]] + mbcnt(m[ev[j]]);
-            a.comb_row[(int64_t)t * k + j] = qv[j];
-        }
+    for (int j = 0; j < KMAX; ++j) qv[j] = j < k ? wb[ev[j]] + mbcnt(m[ev[j]]) : 0;
+    if ((k & 3) == 0) {
+#pragma unroll
+        for (int j = 0; j < KMAX; j += 4)
+            if (j < k) {
+                const i32x4 v = {qv[j], qv[j + 1], qv[j + 2], qv[j + 3]};
+                *(i32x4*)(a.comb_row + (int64_t)t * k + j) = v;
+            }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (j < k) a.comb_row[(int64_t)t * k + j] = qv[j];
     }
     // Sort the (expert, row) pairs by expert id.  rank = expert / Epr is
     // monotone in the id, so the sorted list visits the token's ranks in
@@ -340,28 +397,30 @@ __global__ __launch_bounds__(kWave) void plan_place_kernel(PlaceArgs a)
             qv[j - 1] = sw ? q1 : q0;
             qv[j] = sw ? q0 : q1;
         }
-    int slot = -1, prev_r = -1, p = 0, nd = 0;
+    // The rank rows of the token and each one's expert rows (-1 padded to D
+    // and KR).  Rows of width 4n are written a 16-byte group at a time from
+    // a pending group in registers.
+    RowWriter rank_rows(a.tok_rank_row + (int64_t)t * KR, KR);
+    RowWriter targets(a.fan_dst, D);
+    int prev_r = -1, p = 0;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
         if (j < k) {
             const int r = fdiv(ev[j], a.epr);
             if (r != prev_r) {
-                if (slot >= 0)
-                    for (int i = nd; i < D; ++i) a.fan_dst[(int64_t)p * D + i] = -1;
-                ++slot;
+                if (prev_r >= 0) targets.finish();
                 p = wb[E + r] + mbcnt(m[E + r]);
-                a.tok_rank_row[(int64_t)t * KR + slot] = p;
+                rank_rows.put(p);
                 a.send_token[p] = t;
-                nd = 0;
+                targets.start(a.fan_dst + (int64_t)p * D);
                 prev_r = r;
             }
             a.fan_src[qv[j]] = p;
-            a.fan_dst[(int64_t)p * D + nd] = qv[j];
-            ++nd;
+            targets.put(qv[j]);
         }
     }
-    for (int i = nd; i < D; ++i) a.fan_dst[(int64_t)p * D + i] = -1;
-    for (int i = slot + 1; i < KR; ++i) a.tok_rank_row[(int64_t)t * KR + i] = -1;
+    targets.finish();
+    rank_rows.finish();
 }
 
 hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)

@@ -775,7 +775,7 @@ __device__ __forceinline__ int range_prefix(const RangeArgs& g, int r, int tile)
     return tile < 0 ? g.col_total[g.E + r] : g.tile_base[(int64_t)(g.E + r) * g.ntiles + tile];
 }
 
-template <int U, bool FULL>
+template <int U, bool FULL, int L>
 __global__ __launch_bounds__(kBlock) void dispatch_fanout_range_kernel(const u32x4* __restrict__ src,
                                                                        u32x4* __restrict__ dst,
                                                                        const int32_t* __restrict__ fan_dst, int D,
@@ -806,34 +806,47 @@ __global__ __launch_bounds__(kBlock) void dispatch_fanout_range_kernel(const u32
     if (threadIdx.x == 0) s_pre[R] = carry;
     __syncthreads();
 
+    // L rounds of units per block share the table; a row's target list is
+    // one vector load (lane d holds target d), read back with readlane.
     const int wave = wave_id(), lane = lane_id();
-    const int u = (int)blockIdx.x * kWavesPerBlock + wave;
-    const int l = fdiv(u, rs.div);
-    if (l >= carry) return;
-    int lo = 0, hi = R - 1;  // largest r with s_pre[r] <= l
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_pre[mid] <= l) lo = mid;
-        else hi = mid - 1;
-    }
-    const int p = __builtin_amdgcn_readfirstlane(s_start[lo] + (l - s_pre[lo]));
     const int V = rs.V;
-    const int c0 = (u - l * rs.cpr) * (kWave * U);
-    const u32x4* sp = src + (int64_t)p * V + c0;
-    u32x4 v[U];
-#pragma unroll
-    for (int i = 0; i < U; ++i)
-        if (FULL || c0 + i * kWave + lane < V) v[i] = load_row16<MS_FANOUT_NT_LOAD>(sp + i * kWave + lane);
-    const int32_t* targets = fan_dst + (int64_t)p * D;
-    for (int d = 0; d < D; ++d) {
-        const int q = __builtin_amdgcn_readfirstlane(targets[d]);
-        if (q < 0) break;
-        u32x4* o = dst + (int64_t)q * V + c0;
+#pragma unroll 1
+    for (int round = 0; round < L; ++round) {
+        const int u = (round * (int)gridDim.x + (int)blockIdx.x) * kWavesPerBlock + wave;
+        const int l = fdiv(u, rs.div);
+        if (l >= carry) return;  // later rounds only go further
+        int lo = 0, hi = R - 1;  // largest r with s_pre[r] <= l
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_pre[mid] <= l) lo = mid;
+            else hi = mid - 1;
+        }
+        const int p = __builtin_amdgcn_readfirstlane(s_start[lo] + (l - s_pre[lo]));
+        const int c0 = (u - l * rs.cpr) * (kWave * U);
+        const u32x4* sp = src + (int64_t)p * V + c0;
+        u32x4 v[U];
 #pragma unroll
         for (int i = 0; i < U; ++i)
-            if (FULL || c0 + i * kWave + lane < V) store_row16<MS_FANOUT_NT_STORE>(v[i], o + i * kWave + lane);
+            if (FULL || c0 + i * kWave + lane < V) v[i] = load_row16<MS_FANOUT_NT_LOAD>(sp + i * kWave + lane);
+        const int tv = lane < D ? fan_dst[(int64_t)p * D + lane] : -1;
+        for (int d = 0; d < D; ++d) {
+            const int q = __builtin_amdgcn_readlane(tv, d);
+            if (q < 0) break;
+            u32x4* o = dst + (int64_t)q * V + c0;
+#pragma unroll
+            for (int i = 0; i < U; ++i)
+                if (FULL || c0 + i * kWave + lane < V) store_row16<MS_FANOUT_NT_STORE>(v[i], o + i * kWave + lane);
+        }
     }
 }
+
+// Rounds per block of the range fan-out: the per-block rank table is built
+// once for L rounds of units.  Measured on the MI355X (dispatch of a batch
+// in 4 token chunks, DeepSeek-V3-like): 550 us at one round, 476 us at four,
+// against 440 us for the whole batch in one call.
+#ifndef MS_RANGE_ROUNDS
+#define MS_RANGE_ROUNDS 4
+#endif
 
 hipError_t launch_fanout_range(const void* xr, void* xe, const int32_t* fan_dst, int D, const int32_t* rank_offset,
                                const int32_t* tile_base, const int32_t* col_total, int E, int R, int ntiles, int t0,
@@ -849,16 +862,18 @@ hipError_t launch_fanout_range(const void* xr, void* xe, const int32_t* fan_dst,
     g.E = E; g.R = R; g.ntiles = ntiles;
     g.tile0 = t0 / kPlanTile;
     g.tile1 = t1 == T ? -1 : t1 / kPlanTile;
-    const dim3 grid(grid_for(bound * rs.cpr, kWavesPerBlock));
+    constexpr int L = MS_RANGE_ROUNDS;
+    const int64_t ublocks = (bound * rs.cpr + kWavesPerBlock - 1) / kWavesPerBlock;
+    const dim3 grid((unsigned)((ublocks + L - 1) / L));
     const size_t lds = sizeof(int) * (2 * (size_t)R + 1);
     const u32x4* sp = (const u32x4*)xr;
     u32x4* dp = (u32x4*)xe;
     if (V % kWave == 0)
-        hipLaunchKernelGGL((dispatch_fanout_range_kernel<1, true>), grid, dim3(kBlock), lds, s, sp, dp, fan_dst, D, g,
-                           rs, status);
-    else
-        hipLaunchKernelGGL((dispatch_fanout_range_kernel<1, false>), grid, dim3(kBlock), lds, s, sp, dp, fan_dst, D,
+        hipLaunchKernelGGL((dispatch_fanout_range_kernel<1, true, L>), grid, dim3(kBlock), lds, s, sp, dp, fan_dst, D,
                            g, rs, status);
+    else
+        hipLaunchKernelGGL((dispatch_fanout_range_kernel<1, false, L>), grid, dim3(kBlock), lds, s, sp, dp, fan_dst,
+                           D, g, rs, status);
     return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@
 namespace ms {
 
 constexpr int kWave = 64;          // CDNA wavefront width
-constexpr int kBlock = 256;        // threads per block for every kernel
+constexpr int kBlock = 256;        // threads per block (the plan kernels run one wave per block)
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kPlanTile = kWave;   // tokens per plan tile: one wave, one lane per token
 constexpr int kMaxTopK = 64;

@@ -22,8 +22,14 @@
 //                 destination-local map).
 //   combine_rows  k rows in, one row out: fp32 fused multiply-add in
 //                 ascending slot order, one round-to-nearest-even to bf16
-//                 (DySHARP write-up, section 2 / Fig. 1: combine).
-// Index tiles (target lists, combine rows and gates) are staged per wave in
+//                 (DySHARP write-up, section 2 / Fig. 1: combine).  The same
+//                 body sums expert rows per rank row (receiver) and rank rows
+//                 per token (sender) for the training direction and the
+//                 rank-partial combine.
+//   token ranges  dispatch and combine of a token range, for pipelining.
+//   combine backward  grad_ye rows and the gate-gradient partials, in two
+//                 passes.
+// Index tiles (target lists, combine rows and gates) are staged per block in
 // LDS with one coalesced load and broadcast from there as scalars.
 #include <hip/hip_runtime.h>
 
@@ -484,9 +490,12 @@ hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)
 // 16-byte row traffic, with or without the non-temporal hint.  Which side of
 // which kernel carries the hint was chosen by measurement on the MI355X (the
 // hint changes how lines are kept in L2 and the memory-side cache):
-//   send     plain loads, plain stores (its scattered row writes go through L2)
-//   fan-out  non-temporal loads and stores
-//   combine  non-temporal loads and stores
+//   send              plain loads, plain stores (its scattered row writes go
+//                     through L2)
+//   fan-out           non-temporal loads and stores
+//   combine           non-temporal loads and stores
+//   receiver, sender  non-temporal loads and stores
+//   combine backward  plain loads, non-temporal stores
 // (DeepSeek-V3-like workload: send 153 us with plain stores against 178 us
 // with non-temporal ones; fan-out 303 us against 324 us with plain loads.)
 #ifndef MS_SEND_NT_LOAD
@@ -1248,10 +1257,11 @@ hipError_t launch_sum_rank_rows(const void* src, int64_t src_rows, const int32_t
 // ascending order.  Each bf16 x bf16 product is exact in fp32.
 
 // PART selects the work: 1 = the grad_ye rows, 2 = the gate-gradient
-// partials.  Two passes: a write-heavy one (read grad_out, write k rows)
-// and a read-only one (read grad_out and k rows) ran 366 us against 423 us
-// for one pass doing both (DeepSeek-V3-like workload, MI355X), whose mix
-// of k row reads and k row writes per token kept HBM from streaming.
+// partials.  Two passes, a write-heavy one (read grad_out, write k rows)
+// and a read-only one (read grad_out and k rows), against one pass doing
+// both, whose mix of k row reads and k row writes per token keeps HBM from
+// streaming: 1717 us against 1841 us (long prefill), 775 against 792 us
+// (skewed), 436 us either way (DeepSeek-V3-like), on the MI355X.
 template <int U, bool FULL, int PART>
 __device__ __forceinline__ void combine_bwd_rows(int* s_tile, const u32x4* __restrict__ grad_out,
                                                  const u32x4* __restrict__ ye, const float* __restrict__ w,
@@ -1380,15 +1390,18 @@ __global__ __launch_bounds__(kBlock) void gate_grad_kernel(const float* __restri
     grad_w[i] = acc;
 }
 
-// Vectors per lane of a unit in the two passes (measured on the MI355X,
-// DeepSeek-V3-like workload: grad_ye 182 us at U = 1 against 218 us at
-// U = 2; the partials 180 us at U = 2 against 243 us at U = 1).
+// Vectors per lane of a unit in the two passes, chosen on whole backward
+// steps on the MI355X: grad_ye at U = 1 with the partials at U = 2 ran
+// 1.444 ms (skewed) and 3.840 ms (long prefill) against 1.472 and 3.898 ms
+// with U = 2 for both, and 1.48 and 3.96 ms for one fused pass at U = 1.
 #ifndef MS_CBWD_GRAD_UNIT
 #define MS_CBWD_GRAD_UNIT 1
 #endif
 #ifndef MS_CBWD_DOT_UNIT
 #define MS_CBWD_DOT_UNIT 2
 #endif
+// Pass order: grad_ye first.  The partials first measured 0.900 against
+// 0.878 ms per backward step (DeepSeek-V3-like).
 #ifndef MS_CBWD_DOT_FIRST
 #define MS_CBWD_DOT_FIRST 0
 #endif

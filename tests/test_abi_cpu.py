@@ -89,3 +89,23 @@ def test_product_package_does_not_reach_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
+
+
+def test_header_is_c_and_host_entry_points_link_from_c(tmp_path):
+    """The header compiles as pedantic C99 and a C program linked to the
+    library gets the declared results from the host-only entry points."""
+    import shutil
+    import subprocess
+    import moe_expert_token_amd as ms
+    ms.load()  # raises if the library is not built
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    libdir = os.path.dirname(ms.LIB_PATH)
+    exe = str(tmp_path / "abi_host_check")
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c", "abi_host_check.c"),
+                    "-L", libdir, "-lmoe_shuffle", "-Wl,-rpath," + libdir, "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "ok"

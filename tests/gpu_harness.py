@@ -74,13 +74,15 @@ def compare_plan(g: dict, o: dict):
         np.testing.assert_array_equal(g[key], o[key], err_msg=f"plan array {key}")
 
 
-def check_case(idx, x, w, H, E, R, ye=None, name=""):
+def check_case(idx, x, w, H, E, R, ye=None, name="", query_first=True):
     """Full parity of one case: plan and dispatch bit-exact, combine <= 1 ulp
-    (0 expected), rank rows past N untouched."""
+    (0 expected), rank rows past N untouched.  query_first=False launches the
+    fan-out on the host-side bound T*min(k,R) without a sync, as the bench
+    does."""
     T, k = idx.shape
     orc = oracle.get()
-    say(f"[case] {name} T={T} H={H} E={E} k={k} R={R}")
-    g = run_hip(idx, x, w, H, E, R, ye)
+    say(f"[case] {name} T={T} H={H} E={E} k={k} R={R} query_first={query_first}")
+    g = run_hip(idx, x, w, H, E, R, ye, query_first=query_first)
     assert g["status"] == 0
     rc, o = orc.plan(idx, H, E, R)
     assert rc == 0

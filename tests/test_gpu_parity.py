@@ -35,9 +35,15 @@ def test_config_full_size(cfg_id):
     inp = synth.make_inputs(cfg, 0)
     ye = synth.make_expert_outputs(cfg, 0)
     h = harness()
-    g, o = h.check_case(inp["topk_idx"], inp["x"], inp["topk_w"], cfg.H, cfg.E, cfg.R, ye=ye, name=cfg.name)
+    # the bench's launch configuration: no host sync, fan-out grid on the bound
+    g, o = h.check_case(inp["topk_idx"], inp["x"], inp["topk_w"], cfg.H, cfg.E, cfg.R, ye=ye, name=cfg.name,
+                        query_first=False)
     # the round trip returns x (with -0 read as +0)
     np.testing.assert_array_equal(g["out_rt"], np.where(inp["x"] == 0x8000, 0, inp["x"]).astype(np.uint16))
+    # after a query the fan-out grid is the exact N: the same bits
+    q = h.run_hip(inp["topk_idx"], inp["x"], inp["topk_w"], cfg.H, cfg.E, cfg.R, ye, query_first=True)
+    for key in ("xr", "xe", "out", "out_rt"):
+        np.testing.assert_array_equal(q[key], g[key], err_msg=key)
 
 
 RAGGED = [

@@ -1,0 +1,89 @@
+"""bench.py's host-side logic, on the CPU: the one-GPU guard, the counter
+summary (FETCH_SIZE / WRITE_SIZE scaled by the runtime copy kernel of known
+size), and the rule that a stored traffic figure is used only while the
+kernel source is the one that was profiled."""
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import synth  # noqa: E402
+
+FANOUT = ("void ms::dispatch_fanout_kernel<1, true, 4, 2>(unsigned int __vector(4) const*, "
+          "unsigned int __vector(4)*, int const*, int, long, int const*, ms::RowSplit, int const*)")
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def _counter_csv(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, (name, counter, value) in enumerate(rows):
+            w.writerow([i + 1, name, counter, value])
+
+
+def test_counter_summary_scales_by_the_copy_kernel(tmp_path):
+    cfg = synth.CONFIGS[0]
+    copy_bytes = min(cfg.T * cfg.k * cfg.H * 2, 2 << 30)
+    # the copy reads copy_bytes / 2 KiB on FETCH_SIZE (scale 2) and copy_bytes KiB on WRITE_SIZE (scale 1)
+    fetch_kib, write_kib = 100.0, 30.0
+    _counter_csv(tmp_path / "fetch.csv", [(COPY, "FETCH_SIZE", copy_bytes / 2 / 1024),
+                                          (FANOUT, "FETCH_SIZE", fetch_kib), (FANOUT, "FETCH_SIZE", fetch_kib)])
+    _counter_csv(tmp_path / "write.csv", [(COPY, "WRITE_SIZE", copy_bytes / 1024),
+                                          (FANOUT, "WRITE_SIZE", write_kib), (FANOUT, "WRITE_SIZE", write_kib)])
+    with open(tmp_path / "stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        w.writerow([FANOUT, 2, 2000, 1000.0, 100, 900, 1100, 0])
+    out = tmp_path / "out"
+    out.mkdir()
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--pmc-summary", "--config", "0",
+                        "--src-sha", "0123456789abcdef", "--fetch-csv", str(tmp_path / "fetch.csv"),
+                        "--write-csv", str(tmp_path / "write.csv"), "--trace-stats", str(tmp_path / "stats.csv"),
+                        "--out-dir", str(out)], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    rec = json.load(open(out / f"traffic_dispatch_fanout_kernel_{cfg.name}.json"))
+    assert rec["fetch_scale"] == pytest.approx(2.0)
+    assert rec["write_scale"] == pytest.approx(1.0)
+    assert rec["hbm_bytes_per_launch"] == round(fetch_kib * 1024 * 2 + write_kib * 1024)
+    idx, _ = synth.make_routing(cfg, 0)
+    N = bench.n_rank_rows(idx, cfg.E, cfg.R)
+    assert rec["alg_bytes_per_launch"] == bench.algorithmic_bytes(cfg.T, cfg.H, cfg.k, N)["fanout"]
+    assert rec["kernel_src_sha256_16"] == "0123456789abcdef"
+    assert (out / f"kernels_{cfg.name}.md").exists()
+
+
+def test_stored_traffic_is_used_only_for_the_profiled_source(tmp_path, monkeypatch):
+    (tmp_path / "profiles").mkdir()
+    path = tmp_path / "profiles" / "traffic_dispatch_fanout_kernel_w.json"
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    json.dump({"kernel_src_sha256_16": bench.source_digest(), "hbm_bytes_per_launch": 1234}, open(path, "w"))
+    assert bench.load_traffic("w", "fanout") == 1234
+    json.dump({"kernel_src_sha256_16": "not-this-source", "hbm_bytes_per_launch": 1234}, open(path, "w"))
+    assert bench.load_traffic("w", "fanout") is None
+    assert bench.load_traffic("absent", "fanout") is None
+
+
+def test_algorithmic_bytes_count_each_step_once():
+    # T = 1, H = 8 (16-byte rows), k = 2 experts on N = 2 ranks: every term by hand
+    b = bench.algorithmic_bytes(1, 8, 2, 2)
+    row = 16
+    assert b["send"] == row * (1 + 2) + 4 * 2           # read x once, write 2 rank rows, 2 indices
+    assert b["fanout"] == row * (2 + 2) + 4 * 2         # read 2 rank rows, write 2 expert rows
+    assert b["combine"] == row * (2 + 1) + 8 * 2        # read 2 expert rows, write 1, rows + gates
+    assert b["total"] == b["send"] + b["fanout"] + b["combine"]

@@ -22,7 +22,7 @@
  *    position plus a list of targets; each destination maps it to its own
  *    local layout).
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *  - experts sit on ranks in contiguous blocks: rank(e) = e / (E/R);
  *  - rows inside every rank and expert segment are in ascending token order;
  *  - a (token, rank) pair is sent once even when several of the token's

@@ -1,4 +1,4 @@
-"""The forward step (plan, dispatch, combine) and the combine backward
+"""Stream and graph use.  The forward step (plan, dispatch, combine) and the combine backward
 captured once in a HIP graph and replayed: every replay must give the
 bits of the same calls run eagerly, with eager work and synchronisations
 between the replays.  The library records no memset or host copy in these
@@ -110,3 +110,51 @@ def test_combine_backward_replays_in_a_graph():
         assert torch.equal(gye, want_gye), f"replay {replay}: grad_ye"
         assert torch.equal(gw.view(torch.int32), want_gw.view(torch.int32)), f"replay {replay}: grad_w"
     ms.moe_shuffle_plan_destroy(plan)
+
+
+def test_two_plans_on_two_streams_at_once():
+    """Two independent shuffles, each with its own workspace and buffers,
+    issued on two streams without waits between them, give the bits each
+    gives alone on the default stream."""
+    import torch
+    import moe_expert_token_amd as ms
+    import gpu_harness as h
+    shapes = [(900, 1032, 32, 4, 8), (700, 2048, 64, 6, 16)]
+    rng = np.random.default_rng(23)
+    problems = []
+    for T, H, E, k, R in shapes:
+        idx, w = synth.random_routing(rng, T, E, k, signed_gates=True)
+        x = synth.random_bf16(rng, (T, H))
+        dims = ms.dims_of(T, H, E, k, R)
+        problems.append(dict(
+            dims=dims, idx=torch.from_numpy(idx).cuda(), w=torch.from_numpy(w).cuda(), x=h.to_dev16(x),
+            ws=torch.empty(ms.moe_shuffle_workspace_size(dims), dtype=torch.uint8, device="cuda"),
+            xr=torch.zeros((T * min(k, R), H), dtype=torch.int16, device="cuda"),
+            xe=torch.zeros((T * k, H), dtype=torch.int16, device="cuda"),
+            out=torch.zeros((T, H), dtype=torch.int16, device="cuda")))
+
+    def run(p, stream):
+        plan = ms.moe_shuffle_plan(p["dims"], p["idx"], p["ws"], stream=stream)
+        ms.moe_shuffle_dispatch(plan, p["x"], p["xr"], p["xe"], stream=stream)
+        ms.moe_shuffle_combine(plan, p["xe"], p["w"], p["out"], stream=stream)
+        return plan
+
+    want = []
+    for p in problems:
+        plan = run(p, None)
+        torch.cuda.synchronize()
+        n = ms.moe_shuffle_plan_query(plan)["N"]
+        want.append((n, p["xr"][:n].clone(), p["xe"].clone(), p["out"].clone()))
+        ms.moe_shuffle_plan_destroy(plan)
+    for p in problems:
+        for t in (p["xr"], p["xe"], p["out"]):
+            t.zero_()
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        plans = [run(p, s) for p, s in zip(problems, streams)]
+        torch.cuda.synchronize()
+        for p, plan, (n, xr, xe, out) in zip(problems, plans, want):
+            assert ms.moe_shuffle_plan_query(plan)["N"] == n
+            assert torch.equal(p["xr"][:n], xr) and torch.equal(p["xe"], xe) and torch.equal(p["out"], out)
+            ms.moe_shuffle_plan_destroy(plan)

@@ -568,12 +568,18 @@ def main():
         os.sched_setaffinity(0, {allowed[0]})  # the oracle is single-threaded: pin it to one core
         try:
             reps, tcpu = 0, 0.0
+            parts = {"plan": [], "dispatch": [], "combine": []}
             while reps == 0 or (tcpu < args.cpu_budget_s and reps < 20):
                 s0 = time.perf_counter()
                 rc, o = orc.plan(inp["topk_idx"], H, E, R)
+                s1 = time.perf_counter()
                 oxr, oxe = orc.dispatch(o, inp["x"], E, k, R)
+                s2 = time.perf_counter()
                 orc.combine(o["comb_row"], oxe, inp["topk_w"], E, R)
-                tcpu += time.perf_counter() - s0
+                s3 = time.perf_counter()
+                for key, dt in (("plan", s1 - s0), ("dispatch", s2 - s1), ("combine", s3 - s2)):
+                    parts[key].append(dt)
+                tcpu += s3 - s0
                 reps += 1
         finally:
             os.sched_setaffinity(0, set(allowed))
@@ -582,7 +588,8 @@ def main():
                "sample": f"the full {cfg.name} workload, {reps} pass(es) of plan+dispatch+combine, "
                          f"single-threaded C oracle pinned to one core, {t_rep:.2f} s per pass",
                "tokens_per_s": round(T / t_rep, 1), "host_cpus": os.cpu_count(),
-               "host_cpus_allowed": len(allowed), "cpu_model": cpu_model()}
+               "host_cpus_allowed": len(allowed), "cpu_model": cpu_model(),
+               "median_s": {key: round(float(np.median(v)), 4) for key, v in parts.items()}}
         log(f"[bench] cpu oracle: {cpu}")
 
     # dominant kernel by algorithmic bytes: the receiver fan-out

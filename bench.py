@@ -28,7 +28,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
 METRIC = "dispatch+combine effective HBM GB/s (fraction of peak) and tokens/s, 1 GPU"
-KERNEL_SRC = os.path.join(ROOT, "moe_expert_token_amd", "csrc", "shuffle_kernels.hip")
+KERNEL_DIR = os.path.join(ROOT, "moe_expert_token_amd", "csrc")
+KERNEL_SRCS = ("device_common.h", "plan.hip", "rows.hip", "reduce.hip", "combine_bwd.hip")
 
 
 def log(*a):
@@ -62,7 +63,11 @@ def cpu_model() -> str:
 
 
 def source_digest() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel sources (the files that hold device code)."""
+    h = hashlib.sha256()
+    for name in KERNEL_SRCS:
+        h.update(name.encode() + b"\0" + open(os.path.join(KERNEL_DIR, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 KERNEL_NAMES = {"plan": "plan_count/scan/place", "send": "dispatch_send_kernel",

@@ -1,6 +1,7 @@
 // abi.hip -- the extern "C" boundary: argument checks, workspace layout,
 // launches and error mapping.  Everything that touches data runs in the
-// kernels of shuffle_kernels.hip; this file only validates and launches.
+// kernels (plan.hip, rows.hip, reduce.hip, combine_bwd.hip); this file only
+// validates and launches.
 #include <hip/hip_runtime.h>
 
 #include <stdlib.h>

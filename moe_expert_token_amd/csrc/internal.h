@@ -1,5 +1,5 @@
 // internal.h -- workspace layout and kernel launchers shared by abi.hip and
-// shuffle_kernels.hip (library-internal; not part of the C ABI).
+// the kernel files (library-internal; not part of the C ABI).
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -1,0 +1,378 @@
+// plan.hip -- the routing plan (FUSCO abstract: the light-weight planner
+// that drops redundant sends; press summary, Group 3: logical segments).
+//   plan_count  one wave per 64-token tile; the wave ORs its lanes' bits
+//               into one 64-bit LDS mask per expert and per rank, so a token
+//               with several experts on one rank sets that rank's bit once
+//               (the send-once rule) and no result depends on the order of
+//               the atomics.  Counts are popcounts of the masks.
+//   plan_scan   one block per histogram column: exclusive scan over the
+//               tiles.
+//   plan_place  recomputes the masks, scans the column totals into
+//               offsets, and gives every (token, rank) and (token, expert)
+//               pair its row: tile base + mbcnt(mask).  Rows come out in
+//               ascending token order inside every segment.
+#include "device_common.h"
+
+namespace ms {
+
+// ---------------------------------------------------------------- plan_count
+
+// One wave per 64-token tile.  hist is column-major [(C+1)][ntiles];
+// column C holds the tile's error flag.
+template <int KMAX>
+__global__ __launch_bounds__(kWave) void plan_count_kernel(const int32_t* __restrict__ idx, int T, int k,
+                                                           int E, FastDiv epr, int C, int ntiles,
+                                                           int32_t* __restrict__ hist)
+{
+    extern __shared__ unsigned long long s_mask[];  // [C]
+    const int lane = threadIdx.x;
+    const int tile = blockIdx.x;
+    const int t = tile * kPlanTile + lane;
+
+    // The ids first (their load overlaps the clearing of the masks).
+    int ev[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) ev[j] = -1;
+    if (t < T) {
+        const int32_t* row = idx + (int64_t)t * k;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (j < k) ev[j] = row[j];
+    }
+    for (int i = lane; i < C; i += kWave) s_mask[i] = 0ull;
+    __syncthreads();
+
+    int bad = 0, nslots = 0;
+    if (t < T) {
+        const unsigned long long bit = 1ull << lane;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            if (j < k) {
+                const int e = ev[j];
+                if ((unsigned)e >= (unsigned)E) {
+                    bad = 1;
+                } else {
+                    ++nslots;
+                    atomicOr(&s_mask[e], bit);
+                    atomicOr(&s_mask[E + fdiv(e, epr)], bit);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    int ecount = 0;
+    for (int c = lane; c < C; c += kWave) {
+        const int cnt = __popcll(s_mask[c]);
+        hist[(int64_t)c * ntiles + tile] = cnt;
+        if (c < E) ecount += cnt;
+    }
+    // A token that names one expert twice sets that expert's bit once, so
+    // the expert popcounts fall short of the in-range slots.
+    const bool any_bad = __ballot(bad) != 0ull;
+    const int slots = wave_sum(nslots), placed = wave_sum(ecount);
+    if (lane == 0) hist[(int64_t)C * ntiles + tile] = (any_bad || placed != slots) ? 1 : 0;
+}
+
+// ---------------------------------------------------------------- plan_scan
+
+// Block c < C: exclusive scan of column c over the tiles.  Block C: status.
+__global__ __launch_bounds__(kBlock) void plan_scan_kernel(const int32_t* __restrict__ hist, int ntiles, int C,
+                                                           int32_t* __restrict__ tile_base,
+                                                           int32_t* __restrict__ col_total,
+                                                           int32_t* __restrict__ status)
+{
+    __shared__ int s_wsum[kWavesPerBlock];
+    const int c = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (c == C) {
+        int bad = 0;
+        for (int i = tid; i < ntiles; i += kBlock) bad |= hist[(int64_t)C * ntiles + i];
+        bad = __syncthreads_or(bad);
+        if (tid == 0) status[0] = bad ? MOE_SHUFFLE_E_BAD_INDEX : MOE_SHUFFLE_OK;
+        return;
+    }
+    const int32_t* col = hist + (int64_t)c * ntiles;
+    int32_t* out = tile_base + (int64_t)c * ntiles;
+    int carry = 0;
+    for (int base = 0; base < ntiles; base += kBlock) {
+        const int i = base + tid;
+        const int v = i < ntiles ? col[i] : 0;
+        int total;
+        const int incl = block_inclusive_scan(v, s_wsum, &total);
+        if (i < ntiles) out[i] = carry + incl - v;
+        carry += total;
+    }
+    if (tid == 0) col_total[c] = carry;
+}
+
+// ---------------------------------------------------------------- plan_place
+
+struct PlaceArgs {
+    const int32_t* idx;
+    int T, k, E, R, Epr, KR, D, C, ntiles;
+    FastDiv epr;
+    const int32_t* tile_base;
+    const int32_t* col_total;
+    const int32_t* status;
+    int32_t *expert_count, *expert_offset, *rank_count, *rank_offset;
+    int32_t *send_token, *tok_rank_row, *fan_src, *fan_dst, *comb_row;
+    int32_t *rank_segs, *expert_segs, *n_rank_rows;
+};
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Writes one lane's index row of `width` entries, -1 padded: with width a
+// multiple of 4, in 16-byte groups (the row start is 16-byte aligned);
+// otherwise one entry at a time.
+struct RowWriter {
+    int32_t* row;
+    int width, n;
+    bool vec;
+    i32x4 pend;
+
+    __device__ RowWriter(int32_t* r, int w) : row(r), width(w), n(0), vec((w & 3) == 0), pend{-1, -1, -1, -1} {}
+    __device__ void start(int32_t* r)
+    {
+        row = r;
+        n = 0;
+        pend = i32x4{-1, -1, -1, -1};
+    }
+    __device__ void put(int v)
+    {
+        if (vec) {
+            const int i = n & 3;
+            pend.x = i == 0 ? v : pend.x;
+            pend.y = i == 1 ? v : pend.y;
+            pend.z = i == 2 ? v : pend.z;
+            pend.w = i == 3 ? v : pend.w;
+            if (i == 3) {
+                *(i32x4*)(row + (n & ~3)) = pend;
+                pend = i32x4{-1, -1, -1, -1};
+            }
+        } else {
+            row[n] = v;
+        }
+        ++n;
+    }
+    __device__ void finish()
+    {
+        if (vec) {
+            int g = n & ~3;
+            if (n & 3) {
+                *(i32x4*)(row + g) = pend;
+                g += 4;
+            }
+            for (; g < width; g += 4) *(i32x4*)(row + g) = i32x4{-1, -1, -1, -1};
+        } else {
+            for (int i = n; i < width; ++i) row[i] = -1;
+        }
+    }
+};
+
+template <int KMAX>
+__global__ __launch_bounds__(kWave) void plan_place_kernel(PlaceArgs a)
+{
+    extern __shared__ unsigned long long s_dyn[];
+    const int C = a.C, E = a.E, R = a.R;
+    unsigned long long* s_mask = s_dyn;     // [C]
+    int* s_wbase = (int*)(s_mask + C);      // [C]
+
+    const int lane = threadIdx.x;
+    const int tile = blockIdx.x;
+    const int t = tile * kPlanTile + lane;
+    const int k = a.k;
+    constexpr int kCols = kMaxCols / kWave;  // histogram columns per lane
+
+    // Every global load first, so their latencies overlap: the status word,
+    // this lane's top-k ids, and for each column it owns the column total
+    // and this tile's base within the column.
+    const int status = a.status[0];
+    int ev[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) ev[j] = 0x7fffffff;
+    if (t < a.T) {
+        const int32_t* row = a.idx + (int64_t)t * k;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (j < k) ev[j] = row[j];
+    }
+    int ct[kCols], tb[kCols];
+#pragma unroll
+    for (int i = 0; i < kCols; ++i) {
+        const int c = lane + i * kWave;
+        ct[i] = c < C ? a.col_total[c] : 0;
+        tb[i] = c < C ? a.tile_base[(int64_t)c * a.ntiles + tile] : 0;
+    }
+
+    for (int i = lane; i < C; i += kWave) s_mask[i] = 0ull;
+    __syncthreads();
+    if (status != MOE_SHUFFLE_OK) return;
+
+    // This tile's masks.
+    if (t < a.T) {
+        const unsigned long long bit = 1ull << lane;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (j < k) {
+                atomicOr(&s_mask[ev[j]], bit);
+                atomicOr(&s_mask[E + fdiv(ev[j], a.epr)], bit);
+            }
+    }
+
+    // One exclusive scan over all columns, experts first then ranks; a rank
+    // column's segment offset is its prefix minus the expert total.
+    int excl[kCols];
+    int carry = 0, etot = 0;
+#pragma unroll
+    for (int i = 0; i < kCols; ++i) {
+        excl[i] = 0;
+        if (i * kWave < C) {  // uniform
+            const int incl = wave_inclusive_scan(ct[i]);
+            excl[i] = carry + incl - ct[i];
+            carry += __shfl(incl, kWave - 1, kWave);
+            if (i == (E >> 6)) etot = __shfl(excl[i], E & (kWave - 1), kWave);  // uniform
+        }
+    }
+    __syncthreads();  // the masks are complete
+
+    // Segment offsets (tile 0 publishes them) and the first row of every
+    // column for this tile.
+#pragma unroll
+    for (int i = 0; i < kCols; ++i) {
+        const int c = lane + i * kWave;
+        if (i * kWave < C && c < C) {
+            const int off = c < E ? excl[i] : excl[i] - etot;
+            if (tile == 0) {
+                if (c < E) {
+                    a.expert_count[c] = ct[i];
+                    a.expert_offset[c] = off;
+                    int32_t* seg = a.expert_segs + 4 * c;
+                    seg[0] = fdiv(c, a.epr); seg[1] = c; seg[2] = off; seg[3] = ct[i];
+                } else {
+                    const int r = c - E;
+                    a.rank_count[r] = ct[i];
+                    a.rank_offset[r] = off;
+                    int32_t* seg = a.rank_segs + 4 * r;
+                    seg[0] = r; seg[1] = -1; seg[2] = off; seg[3] = ct[i];
+                }
+            }
+            s_wbase[c] = off + tb[i];
+        }
+    }
+    if (tile == 0 && lane == 0) {
+        a.expert_offset[E] = etot;
+        a.rank_offset[R] = carry - etot;
+        a.n_rank_rows[0] = carry - etot;
+    }
+    __syncthreads();
+    if (t >= a.T) return;
+
+    const unsigned long long* m = s_mask;
+    const int* wb = s_wbase;
+    const int KR = a.KR, D = a.D;
+
+    // Expert row of every slot, in slot order.  Index rows whose width is a
+    // multiple of 4 go out as 16-byte stores (a lane's row is contiguous).
+    int qv[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) qv[j] = j < k ? wb[ev[j]] + mbcnt(m[ev[j]]) : 0;
+    if ((k & 3) == 0) {
+#pragma unroll
+        for (int j = 0; j < KMAX; j += 4)
+            if (j < k) {
+                const i32x4 v = {qv[j], qv[j + 1], qv[j + 2], qv[j + 3]};
+                *(i32x4*)(a.comb_row + (int64_t)t * k + j) = v;
+            }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (j < k) a.comb_row[(int64_t)t * k + j] = qv[j];
+    }
+    // Sort the (expert, row) pairs by expert id.  rank = expert / Epr is
+    // monotone in the id, so the sorted list visits the token's ranks in
+    // ascending order and, inside a rank, its experts in ascending order.
+#pragma unroll
+    for (int i = 1; i < KMAX; ++i)
+#pragma unroll
+        for (int j = i; j > 0; --j) {
+            const bool sw = ev[j] < ev[j - 1];
+            const int e0 = ev[j - 1], e1 = ev[j], q0 = qv[j - 1], q1 = qv[j];
+            ev[j - 1] = sw ? e1 : e0;
+            ev[j] = sw ? e0 : e1;
+            qv[j - 1] = sw ? q1 : q0;
+            qv[j] = sw ? q0 : q1;
+        }
+    // The rank rows of the token and each one's expert rows (-1 padded to D
+    // and KR).  Rows of width 4n are written a 16-byte group at a time from
+    // a pending group in registers.
+    RowWriter rank_rows(a.tok_rank_row + (int64_t)t * KR, KR);
+    RowWriter targets(a.fan_dst, D);
+    int prev_r = -1, p = 0;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+            const int r = fdiv(ev[j], a.epr);
+            if (r != prev_r) {
+                if (prev_r >= 0) targets.finish();
+                p = wb[E + r] + mbcnt(m[E + r]);
+                rank_rows.put(p);
+                a.send_token[p] = t;
+                targets.start(a.fan_dst + (int64_t)p * D);
+                prev_r = r;
+            }
+            a.fan_src[qv[j]] = p;
+            targets.put(qv[j]);
+        }
+    }
+    targets.finish();
+    rank_rows.finish();
+}
+
+hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)
+{
+    const int ntiles = L.ntiles;
+    const size_t lds_count = sizeof(unsigned long long) * L.C;
+    const FastDiv epr = make_fastdiv(L.Epr);
+    if (L.k <= 8)
+        hipLaunchKernelGGL(plan_count_kernel<8>, dim3(ntiles), dim3(kWave), lds_count, s, P.idx, L.T, L.k, L.E,
+                           epr, L.C, ntiles, P.tile_hist);
+    else if (L.k <= 16)
+        hipLaunchKernelGGL(plan_count_kernel<16>, dim3(ntiles), dim3(kWave), lds_count, s, P.idx, L.T, L.k, L.E,
+                           epr, L.C, ntiles, P.tile_hist);
+    else if (L.k <= 32)
+        hipLaunchKernelGGL(plan_count_kernel<32>, dim3(ntiles), dim3(kWave), lds_count, s, P.idx, L.T, L.k, L.E,
+                           epr, L.C, ntiles, P.tile_hist);
+    else
+        hipLaunchKernelGGL(plan_count_kernel<64>, dim3(ntiles), dim3(kWave), lds_count, s, P.idx, L.T, L.k, L.E,
+                           epr, L.C, ntiles, P.tile_hist);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(plan_scan_kernel, dim3(L.C + 1), dim3(kBlock), 0, s, P.tile_hist, ntiles, L.C,
+                       P.tile_base, P.col_total, P.status);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    PlaceArgs a;
+    a.idx = P.idx;
+    a.T = L.T; a.k = L.k; a.E = L.E; a.R = L.R; a.Epr = L.Epr; a.KR = L.KR; a.D = L.D; a.C = L.C;
+    a.ntiles = ntiles;
+    a.epr = epr;
+    a.tile_base = P.tile_base; a.col_total = P.col_total; a.status = P.status;
+    a.expert_count = P.expert_count; a.expert_offset = P.expert_offset;
+    a.rank_count = P.rank_count; a.rank_offset = P.rank_offset;
+    a.send_token = P.send_token; a.tok_rank_row = P.tok_rank_row; a.fan_src = P.fan_src;
+    a.fan_dst = P.fan_dst; a.comb_row = P.comb_row;
+    a.rank_segs = P.rank_segs; a.expert_segs = P.expert_segs; a.n_rank_rows = P.n_rank_rows;
+    const size_t lds_place = lds_count + sizeof(int) * L.C;
+    if (L.k <= 8)
+        hipLaunchKernelGGL(plan_place_kernel<8>, dim3(ntiles), dim3(kWave), lds_place, s, a);
+    else if (L.k <= 16)
+        hipLaunchKernelGGL(plan_place_kernel<16>, dim3(ntiles), dim3(kWave), lds_place, s, a);
+    else if (L.k <= 32)
+        hipLaunchKernelGGL(plan_place_kernel<32>, dim3(ntiles), dim3(kWave), lds_place, s, a);
+    else
+        hipLaunchKernelGGL(plan_place_kernel<64>, dim3(ntiles), dim3(kWave), lds_place, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace ms

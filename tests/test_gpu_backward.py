@@ -37,6 +37,7 @@ def test_backward_config_full_size(cfg_id):
 @pytest.mark.parametrize("T,H,E,k,R", [
     (0, 64, 8, 2, 4), (1, 8, 8, 2, 4), (63, 136, 8, 3, 4), (65, 1032, 16, 4, 4), (300, 96, 12, 3, 1),
     (257, 7168, 64, 6, 16), (513, 264, 24, 24, 6), (77, 64, 128, 64, 8), (200, 2048, 32, 8, 32),
+    (333, 64, 16, 1, 4), (50, 32, 1, 1, 1),
 ])
 def test_backward_ragged_shapes(T, H, E, k, R):
     rng = np.random.default_rng(T * 31 + H + E * 3 + k * 5 + R)

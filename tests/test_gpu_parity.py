@@ -62,6 +62,8 @@ RAGGED = [
     (300, 96, 12, 3, 1),      # a single rank
     (129, 128, 1024 - 64, 8, 64),  # the largest histogram (E + R = 1024)
     (77, 64, 128, 64, 8),     # the largest top-k
+    (333, 64, 16, 1, 4),      # top-1: one expert row per token, combine is a scaled copy
+    (50, 32, 1, 1, 1),        # a single expert on a single rank
 ]
 
 

@@ -136,3 +136,29 @@ def test_repeat_runs_bitwise_identical():
         np.testing.assert_array_equal(g["xr"], ref["xr"])
         np.testing.assert_array_equal(g["xe"], ref["xe"])
         np.testing.assert_array_equal(g["out"], ref["out"])
+
+
+def _random_shapes(n=24, seed=77):
+    """Seeded shapes inside the limits: H a multiple of 8, R dividing E,
+    k <= min(E, 64), E + R <= 1024."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < n:
+        R = int(rng.choice([1, 2, 3, 4, 8, 16, 32, 64]))
+        E = R * int(rng.integers(1, 17))
+        if E + R > 1024:
+            continue
+        k = int(rng.integers(1, min(E, 64) + 1))
+        T = int(rng.integers(0, 2500))
+        H = 8 * int(rng.integers(1, 300))
+        shapes.append((T, H, E, k, R))
+    return shapes
+
+
+@pytest.mark.parametrize("T,H,E,k,R", _random_shapes())
+def test_random_shapes(T, H, E, k, R):
+    rng = np.random.default_rng(T * 31 + H * 7 + E * 3 + k + R)
+    idx, w = synth.random_routing(rng, T, E, k, signed_gates=True)
+    x = synth.random_bf16(rng, (T, H))
+    ye = synth.wide_bf16(rng, (T * k, H))
+    harness().check_case(idx, x, w, H, E, R, ye=ye, name=f"random-{T}x{H}", query_first=bool(T % 2))

@@ -46,3 +46,26 @@ def test_backward_ragged_shapes(T, H, E, k, R):
     grad_xe = synth.wide_bf16(rng, (T * k, H), -10, 10)
     grad_out = synth.wide_bf16(rng, (T, H), -10, 10)
     _h().check_backward_case(idx, w, H, E, R, ye, grad_xe, grad_out, name=f"ragged-{T}x{H}")
+
+
+def _random_shapes(n=12, seed=78):
+    rng = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < n:
+        R = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        E = R * int(rng.integers(1, 17))
+        if E + R > 1024:
+            continue
+        k = int(rng.integers(1, min(E, 64) + 1))
+        shapes.append((int(rng.integers(1, 1500)), 8 * int(rng.integers(1, 260)), E, k, R))
+    return shapes
+
+
+@pytest.mark.parametrize("T,H,E,k,R", _random_shapes())
+def test_backward_random_shapes(T, H, E, k, R):
+    rng = np.random.default_rng(T * 13 + H + E * 5 + k * 3 + R)
+    idx, w = synth.random_routing(rng, T, E, k, signed_gates=True)
+    ye = synth.wide_bf16(rng, (T * k, H), -8, 8)
+    grad_xe = synth.wide_bf16(rng, (T * k, H), -8, 8)
+    grad_out = synth.wide_bf16(rng, (T, H), -8, 8)
+    _h().check_backward_case(idx, w, H, E, R, ye, grad_xe, grad_out, name=f"random-{T}x{H}")

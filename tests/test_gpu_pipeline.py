@@ -116,3 +116,34 @@ def test_range_arguments():
     ms.moe_shuffle_dispatch_range(plan, x, xr, xe, 256, 256)   # empty range: nothing to do
     ms.moe_shuffle_dispatch_range(plan, x, xr, xe, 512, 600)   # up to T
     torch.cuda.synchronize()
+
+
+def _random_ranges(n=10, seed=79):
+    """Seeded shapes with random range boundaries on the 64-token tile."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        R = int(rng.choice([1, 2, 4, 8, 16]))
+        E = R * int(rng.integers(1, 9))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        T = int(rng.integers(1, 3000))
+        H = 8 * int(rng.integers(1, 200))
+        cuts = sorted({64 * int(c) for c in rng.integers(1, max(2, -(-T // 64)), size=int(rng.integers(0, 6)))
+                       if 64 * int(c) < T})
+        cases.append((T, H, E, k, R, [0] + cuts + [T]))
+    return cases
+
+
+@pytest.mark.parametrize("T,H,E,k,R,bounds", _random_ranges())
+def test_random_ranges(T, H, E, k, R, bounds):
+    import oracle
+    rng = np.random.default_rng(T + 3 * H + 5 * E + 7 * k + R)
+    idx, w = synth.random_routing(rng, T, E, k, signed_gates=True)
+    x = synth.random_bf16(rng, (T, H))
+    xr, xe, out, N = run_pipelined(idx, x, w, H, E, R, bounds)
+    orc = oracle.get()
+    rc, o = orc.plan(idx, H, E, R)
+    oxr, oxe = orc.dispatch(o, x, E, k, R)
+    np.testing.assert_array_equal(xr[:N], oxr)
+    np.testing.assert_array_equal(xe, oxe)
+    np.testing.assert_array_equal(out, orc.combine(o["comb_row"], oxe, w, E, R))

@@ -162,3 +162,48 @@ def test_random_shapes(T, H, E, k, R):
     x = synth.random_bf16(rng, (T, H))
     ye = synth.wide_bf16(rng, (T * k, H))
     harness().check_case(idx, x, w, H, E, R, ye=ye, name=f"random-{T}x{H}", query_first=bool(T % 2))
+
+
+def test_largest_batch_against_oracle_plan_and_properties():
+    """A batch four times the largest workload's rows (262144 tokens, H = 7168,
+    256 experts, top-8, 32 ranks: xr and xe 30 GB each), in the bench's launch
+    configuration.  The plan is compared bit for bit with the oracle's; the
+    row buffers, too large to copy out, are checked on the device against
+    what the oracle's plan says each row holds (xr[p] = x[send_token[p]],
+    xe[q] = x[token of q]); the identity-expert round trip returns x."""
+    import torch
+    import moe_expert_token_amd as ms
+    import oracle
+    T, H, E, k, R = 262144, 7168, 256, 8, 32
+    rng = np.random.default_rng(262144)
+    idx, w = synth.random_routing(rng, T, E, k)
+    dims = ms.dims_of(T, H, E, k, R)
+    ws = torch.empty(ms.moe_shuffle_workspace_size(dims), dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    x = torch.randn((T, H), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+    xr = torch.empty((T * min(k, R), H), dtype=torch.int16, device="cuda")
+    xe = torch.empty((T * k, H), dtype=torch.int16, device="cuda")
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    w_d = torch.from_numpy(w).cuda()
+    plan = ms.moe_shuffle_plan(dims, torch.from_numpy(idx).cuda(), ws)
+    ms.moe_shuffle_dispatch_send(plan, x, xr)
+    ms.moe_shuffle_dispatch_fanout(plan, xr, xe)
+    ms.moe_shuffle_combine(plan, xe, w_d, out)
+    N = ms.moe_shuffle_plan_query(plan)["N"]
+    torch.cuda.synchronize()
+    rc, o = oracle.get().plan(idx, H, E, R)
+    assert rc == 0 and o["N"] == N
+    v = ms.plan_array_views(plan, N)
+    for key in ("send_token", "tok_rank_row", "fan_src", "fan_dst", "comb_row", "expert_offset", "rank_offset"):
+        np.testing.assert_array_equal(v[key].cpu().numpy(), o[key], err_msg=key)
+    send_token = torch.from_numpy(o["send_token"].astype(np.int64)).cuda()
+    tok_of_q = send_token[torch.from_numpy(o["fan_src"].astype(np.int64)).cuda()]
+    step = 32768
+    for p0 in range(0, N, step):
+        p1 = min(N, p0 + step)
+        assert torch.equal(xr[p0:p1], x[send_token[p0:p1]]), f"xr rows {p0}..{p1}"
+    for q0 in range(0, T * k, step):
+        q1 = min(T * k, q0 + step)
+        assert torch.equal(xe[q0:q1], x[tok_of_q[q0:q1]]), f"xe rows {q0}..{q1}"
+    assert torch.equal(out, torch.where(x == -32768, torch.zeros_like(x), x)), "round trip"
+    ms.moe_shuffle_plan_destroy(plan)

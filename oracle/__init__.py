@@ -60,9 +60,10 @@ class Oracle:
         self.lib.oracle_combine_backward.argtypes = [ctypes.POINTER(_Dims), vp, vp, vp, vp, vp, vp]
         self.lib.oracle_combine_rank_partial.argtypes = [ctypes.POINTER(_Dims), vp, vp, vp, ctypes.c_int32, vp, vp,
                                                          vp, vp]
+        self.lib.oracle_combine_rank_partial_f32.argtypes = self.lib.oracle_combine_rank_partial.argtypes
         for f in (self.lib.oracle_check_dims, self.lib.oracle_plan, self.lib.oracle_dispatch,
                   self.lib.oracle_combine, self.lib.oracle_dispatch_backward, self.lib.oracle_combine_backward,
-                  self.lib.oracle_combine_rank_partial):
+                  self.lib.oracle_combine_rank_partial, self.lib.oracle_combine_rank_partial_f32):
             f.restype = ctypes.c_int
 
     @staticmethod
@@ -187,6 +188,27 @@ class Oracle:
                                                   out.ctypes.data)
         if rc:
             raise RuntimeError(f"oracle_combine_rank_partial: {rc}")
+        return part, out
+
+
+    def combine_rank_partial_f32(self, plan: dict, ye: np.ndarray, w: np.ndarray, E: int, R: int):
+        """Returns (partial [N,H] fp32, out [T,H] bf16 bits): partials kept in fp32."""
+        ye = np.ascontiguousarray(ye, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        T, k = w.shape
+        H = ye.shape[1]
+        N = plan["N"]
+        d = self.dims(T, H, E, k, R)
+        part = np.zeros((N, H), np.float32)
+        out = np.zeros((T, H), np.uint16)
+        fd = np.ascontiguousarray(plan["fan_dst"], dtype=np.int32)
+        tr = np.ascontiguousarray(plan["tok_rank_row"], dtype=np.int32)
+        cr = np.ascontiguousarray(plan["comb_row"], dtype=np.int32)
+        rc = self.lib.oracle_combine_rank_partial_f32(ctypes.byref(d), fd.ctypes.data, tr.ctypes.data,
+                                                      cr.ctypes.data, N, ye.ctypes.data, w.ctypes.data,
+                                                      part.ctypes.data, out.ctypes.data)
+        if rc:
+            raise RuntimeError(f"oracle_combine_rank_partial_f32: {rc}")
         return part, out
 
 

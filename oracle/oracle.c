@@ -382,3 +382,48 @@ int oracle_combine_rank_partial(const oracle_dims* d, const int32_t* fan_dst, co
         }
     return OR_OK;
 }
+
+/*
+ * The same return path with the per-(token, rank) partials kept in fp32
+ * (DySHARP write-up, section 2 / Fig. 1: a device sums its experts' results
+ * for a token before they travel back).  partial[p] = the fp32 fused
+ * multiply-add chain of gate * ye over rank row p's expert rows in ascending
+ * expert row, not rounded; out[t] = bf16 of the fp32 sum, from +0, of
+ * token t's partials in ascending rank.  The only rounding to bf16 is the
+ * last one.
+ */
+int oracle_combine_rank_partial_f32(const oracle_dims* d, const int32_t* fan_dst, const int32_t* tok_rank_row,
+                                    const int32_t* comb_row, int32_t n_rank_rows, const uint16_t* ye,
+                                    const float* w, float* partial, uint16_t* out)
+{
+    int rc = oracle_check_dims(d);
+    if (rc) return rc;
+    const int T = d->num_tokens, k = d->top_k, R = d->num_ranks;
+    const int Epr = d->num_experts / R, KR = imin(k, R), D = imin(k, Epr);
+    const int64_t H = d->hidden, Tk = (int64_t)T * k;
+    float* g = (float*)malloc(sizeof(float) * (size_t)(Tk > 0 ? Tk : 1));
+    if (!g) return OR_E_INVALID_ARG;
+    for (int64_t s = 0; s < Tk; ++s) g[comb_row[s]] = w[s];   /* the gate each expert row carries */
+    for (int64_t p = 0; p < n_rank_rows; ++p)
+        for (int64_t h = 0; h < H; ++h) {
+            float sum = 0.0f;
+            for (int e = 0; e < D; ++e) {
+                const int64_t q = fan_dst[p * D + e];
+                if (q < 0) break;
+                sum = fmaf(g[q], bf16_to_f32(ye[q * H + h]), sum);
+            }
+            partial[p * H + h] = sum;
+        }
+    free(g);
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            float sum = 0.0f;
+            for (int r = 0; r < KR; ++r) {
+                const int64_t p = tok_rank_row[t * KR + r];
+                if (p < 0) break;
+                sum = sum + partial[p * H + h];
+            }
+            out[t * H + h] = f32_to_bf16_rne(sum);
+        }
+    return OR_OK;
+}

@@ -338,6 +338,30 @@ def check_rank_partial_exact(plan, ye, w, part, out):
         np.testing.assert_array_equal(out[t], staged_sum_exact(ps, part))
 
 
+def check_rank_partial_f32_exact(plan, ye, w, part, out):
+    """Exact replay of the fp32-partial return path: each partial is the
+    correctly rounded fp32 fma chain over its expert rows (compared as fp32
+    bits), each output the fp32 running sum of its partials, then bf16."""
+    T, k = plan["comb_row"].shape
+    gate = np.zeros(T * k, np.float32)
+    gate[plan["comb_row"].ravel()] = w.ravel()
+    H = ye.shape[1]
+    for p in range(plan["N"]):
+        qs = [int(q) for q in plan["fan_dst"][p] if q >= 0]
+        for h in range(H):
+            acc = 0.0
+            for q in qs:
+                acc = f32_fma_exact(float(gate[q]), _f(ye[q, h]), acc)
+            assert np.float32(acc).view(np.uint32) == part[p, h].view(np.uint32), (p, h)
+    for t in range(T):
+        ps = [int(p) for p in plan["tok_rank_row"][t] if p >= 0]
+        for h in range(H):
+            acc = 0.0
+            for pp in ps:
+                acc = f32_add_exact(acc, float(part[pp, h]))
+            assert out[t, h] == bf16_bits_of_exact(acc), (t, h)
+
+
 def order_sensitive_backward_case():
     """Tiny plans where summation order decides the bf16 result:
     (a) one token, three experts on one rank: the receiver sums three rows;
@@ -363,6 +387,9 @@ def run_battery_backward(orc) -> None:
         part, out = orc.combine_rank_partial(p, case["g"], w, case["E"], case["R"])
         check_rank_partial_exact(p, case["g"], w, part, out)
         assert float((np.uint32(out[0, 0]) << np.uint32(16)).view(np.float32)) == 2.0 ** -30
+        part32, out32 = orc.combine_rank_partial_f32(p, case["g"], w, case["E"], case["R"])
+        check_rank_partial_f32_exact(p, case["g"], w, part32, out32)
+        assert float((np.uint32(out32[0, 0]) << np.uint32(16)).view(np.float32)) == 2.0 ** -30
     for (T, E, k, R) in ((9, 8, 3, 4), (7, 12, 4, 2), (6, 16, 5, 16)):
         rng = np.random.default_rng(T * 101 + E)
         idx, w = synth.random_routing(rng, T, E, k, signed_gates=True)
@@ -372,6 +399,8 @@ def run_battery_backward(orc) -> None:
         check_dispatch_backward_exact(p, ye, gxr, gx)
         part, out = orc.combine_rank_partial(p, ye, w, E, R)
         check_rank_partial_exact(p, ye, w, part, out)
+        part32, out32 = orc.combine_rank_partial_f32(p, ye, w, E, R)
+        check_rank_partial_f32_exact(p, ye, w, part32, out32)
         g = synth.wide_bf16(rng, (T, 8), -6, 6)
         gye, gw = orc.combine_backward(p["comb_row"], g, ye, w, E, R)
         check_combine_backward(p["comb_row"], g, ye, w, gye, gw)

@@ -136,3 +136,51 @@ def test_combine_backward_adjoint_identity(orc):
     lhs = (exact_out * synth.bf16_bits_to_f32(g)).sum()
     rhs = (w.astype(np.float64) * gw).sum()
     assert abs(lhs - rhs) <= 1e-9 * max(1.0, abs(lhs))
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_rank_partial_f32_exact_replay(orc, seed):
+    rng = np.random.default_rng(60 + seed)
+    T, E, k, R = 6, 16, 5, 4
+    idx, w = synth.random_routing(rng, T, E, k, signed_gates=True)
+    rc, p = orc.plan(idx, 8, E, R)
+    ye = synth.wide_bf16(rng, (T * k, 8), -10, 10)
+    part, out = orc.combine_rank_partial_f32(p, ye, w, E, R)
+    pins.check_rank_partial_f32_exact(p, ye, w, part, out)
+
+
+def test_rank_partial_f32_equals_direct_combine_when_exact(orc):
+    """Power-of-two gates and small integers: nothing rounds, so the fp32
+    partials sum to the direct combine bit for bit."""
+    rng = np.random.default_rng(11)
+    T, E, k, R = 64, 32, 6, 8
+    idx, _ = synth.random_routing(rng, T, E, k)
+    w = (2.0 ** -rng.integers(0, 4, size=(T, k))).astype(np.float32)
+    rc, p = orc.plan(idx, 32, E, R)
+    ye = _int_bf16(rng, (T * k, 32), -4, 4)
+    _, out = orc.combine_rank_partial_f32(p, ye, w, E, R)
+    np.testing.assert_array_equal(out, orc.combine(p["comb_row"], ye, w, E, R))
+
+
+def test_rank_partial_f32_error_bound(orc):
+    """Random values: within one bf16 rounding plus the fp32 chain bound of
+    the exact weighted sum (the partials are not rounded to bf16), and on
+    average no farther from it than the bf16-partial path."""
+    rng = np.random.default_rng(12)
+    T, E, k, R = 128, 64, 8, 8
+    idx, w = synth.random_routing(rng, T, E, k, signed_gates=True)
+    rc, p = orc.plan(idx, 64, E, R)
+    ye = synth.random_bf16(rng, (T * k, 64))
+    part, out = orc.combine_rank_partial_f32(p, ye, w, E, R)
+    yf = synth.bf16_bits_to_f32(ye).astype(np.float64)
+    terms = w.astype(np.float64)[:, :, None] * yf[p["comb_row"]]
+    exact = terms.sum(axis=1)
+    got = synth.bf16_bits_to_f32(out).astype(np.float64)
+    chain = 2 * k * 2.0 ** -24 * np.abs(terms).sum(axis=1)   # fp32 fma chains and the fp32 sum of partials
+    bound = 2.0 ** -8 * (np.abs(exact) + chain) + chain + 2.0 ** -133   # plus one bf16 rounding (half ulp <= 2^-8 rel.)
+    assert np.all(np.abs(got - exact) <= bound)
+    # the fp32 path is at least as close to the exact sum as the bf16-partial path, on average
+    _, out16 = orc.combine_rank_partial(p, ye, w, E, R)
+    e16 = np.abs(synth.bf16_bits_to_f32(out16).astype(np.float64) - exact).mean()
+    e32 = np.abs(got - exact).mean()
+    assert e32 <= e16

@@ -52,6 +52,12 @@ MUTANTS = {
                              "for (int64_t i = 0; i < Tk; ++i) gate[i] = w[i];"),
     "partial_truncates": ("partial[p * H + h] = f32_to_bf16_rne(acc);",
                           "{ uint32_t u_; memcpy(&u_, &acc, 4); partial[p * H + h] = (uint16_t)(u_ >> 16); }"),
+    "partial_f32_rounded_to_bf16": ("            partial[p * H + h] = sum;",
+                                    "            partial[p * H + h] = bf16_to_f32(f32_to_bf16_rne(sum));"),
+    "partial_f32_unfused": ("sum = fmaf(g[q], bf16_to_f32(ye[q * H + h]), sum);",
+                            "sum = sum + g[q] * bf16_to_f32(ye[q * H + h]);"),
+    "partial_f32_ranks_descending": ("for (int r = 0; r < KR; ++r) {\n                const int64_t p = tok_rank_row[t * KR + r];\n                if (p < 0) break;",
+                                     "for (int r = KR - 1; r >= 0; --r) {\n                const int64_t p = tok_rank_row[t * KR + r];\n                if (p < 0) continue;"),
     "flush_subnormals": ("uint32_t u = (uint32_t)b << 16;\n    float f;",
                          "uint32_t u = (uint32_t)b << 16;\n    if ((u & 0x7f800000u) == 0) u &= 0x80000000u;\n    float f;"),
 }

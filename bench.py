@@ -196,8 +196,9 @@ def path_bytes(path, T, H, k, N):
         send = row * (N + T) + 4 * N
         return {"combine_bwd": cbwd, "sum_expert_rows": recv, "sum_rank_rows": send, "total": cbwd + recv + send}
     # rank-partial combine: gate scatter, weighted receiver sum, sender sum
-    recv = row * (T * k + N) + 16 * T * k
-    send = row * (N + T) + 4 * N
+    prow = 2 * row if path == "rank-partial-f32" else row   # fp32 partial rows are twice as wide
+    recv = row * T * k + prow * N + 16 * T * k
+    send = prow * N + row * T + 4 * N
     return {"sum_expert_rows": recv, "sum_rank_rows": send, "total": recv + send}
 
 
@@ -245,10 +246,14 @@ def bench_path(args):
         calls = (lambda: ms.moe_shuffle_combine_backward(plan, next_gout(), ye, w, gye, gw),
                  lambda: ms.moe_shuffle_sum_expert_rows(plan, gxe, None, rows),
                  lambda: ms.moe_shuffle_sum_rank_rows(plan, rows, out))
-    else:
+    elif args.path == "rank-partial":
         names = ("sum_expert_rows", "sum_rank_rows")
         calls = (lambda: ms.moe_shuffle_sum_expert_rows(plan, ye, w, rows),
                  lambda: ms.moe_shuffle_sum_rank_rows(plan, rows, out))
+    else:  # rank-partial-f32: one call, both stages
+        rows32 = torch.empty((T * KR, H), dtype=torch.float32, device=dev)
+        names = ("combine_rank_partial_f32",)
+        calls = (lambda: ms.moe_shuffle_combine_rank_partial_f32(plan, ye, w, rows32, out),)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         for c in calls:
@@ -281,11 +286,18 @@ def bench_path(args):
             parity = {"grad_xr_bitexact": bool(np.array_equal(rows[:N].cpu().numpy().view(np.uint16), o_gxr)),
                       "grad_x_bitexact": bool(np.array_equal(out.cpu().numpy().view(np.uint16), o_gx)),
                       "grad_ye_bitexact": bool(np.array_equal(gye.cpu().numpy().view(np.uint16), o_gye))}
-        else:
+        elif args.path == "rank-partial":
             o_part, o_out = orc.combine_rank_partial(o, ye_h, w_h, E, R)
             parity = {"partial_bitexact": bool(np.array_equal(rows[:N].cpu().numpy().view(np.uint16), o_part)),
                       "out_bitexact": bool(np.array_equal(out.cpu().numpy().view(np.uint16), o_out))}
+        else:
+            o_part, o_out = orc.combine_rank_partial_f32(o, ye_h, w_h, E, R)
+            parity = {"partial_bitexact": bool(np.array_equal(rows32[:N].cpu().numpy().view(np.uint32),
+                                                              o_part.view(np.uint32))),
+                      "out_bitexact": bool(np.array_equal(out.cpu().numpy().view(np.uint16), o_out))}
         log(f"[bench] parity vs oracle: {parity}")
+    if args.path == "rank-partial-f32":
+        B = dict(B, combine_rank_partial_f32=B["total"])
     dom = max(names, key=lambda n: B[n])
     value = B["total"] / (ms_per_step * 1e-3) / 1e9
     rec = {
@@ -406,9 +418,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--chunks", type=int, default=4, help="token chunks for --path pipelined")
-    ap.add_argument("--path", default="forward", choices=("forward", "backward", "rank-partial", "pipelined"),
+    ap.add_argument("--path", default="forward",
+                    choices=("forward", "backward", "rank-partial", "rank-partial-f32", "pipelined"),
                     help="forward (default): plan + dispatch + combine; backward: combine and dispatch backward; "
-                         "rank-partial: combine through one row per (token, rank)")
+                         "rank-partial: combine through one row per (token, rank); rank-partial-f32: the same "
+                         "with fp32 partial rows")
     ap.add_argument("--pmc-summary", action="store_true", help="summarise rocprofv3 CSVs into profiles/ (no GPU)")
     ap.add_argument("--fetch-csv")
     ap.add_argument("--write-csv")

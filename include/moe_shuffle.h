@@ -234,6 +234,17 @@ int moe_shuffle_dispatch_backward(moe_shuffle_plan_t plan, const void* grad_xe, 
 int moe_shuffle_combine_rank_partial(moe_shuffle_plan_t plan, const void* ye, const float* topk_w, void* partial,
                                      int64_t partial_rows, void* out, void* stream);
 
+/* The same return path with the per-(token, rank) partials kept in fp32
+ * (twice the wire bytes of the bf16 partials, one rounding fewer):
+ *   partial[p] = fp32 fma chain of gate * ye over rank row p's expert rows
+ *                (ascending), not rounded;
+ *   out[t]     = bf16( fp32 sum from +0 of t's partials, ascending rank ).
+ * ye [T*k, H] bf16, partial fp32 [partial_rows, H] (partial_rows as for xr
+ * in moe_shuffle_dispatch), out [T, H] bf16, pairwise disjoint; topk_w fp32
+ * [T, k]. */
+int moe_shuffle_combine_rank_partial_f32(moe_shuffle_plan_t plan, const void* ye, const float* topk_w,
+                                         float* partial, int64_t partial_rows, void* out, void* stream);
+
 /* Backward of combine, out[t] = sum_j w[t][j] * ye[comb_row[t][j]]:
  *   grad_ye[comb_row[t][j]] = bf16( fp32(w[t][j] * grad_out[t]) )
  *   grad_w[t][j] = sum over h of grad_out[t][h] * ye[comb_row[t][j]][h] in fp32:

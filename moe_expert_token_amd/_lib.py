@@ -25,7 +25,7 @@ EXPORTS = (
     "moe_shuffle_plan_arrays_get", "moe_shuffle_plan_destroy", "moe_shuffle_strerror",
     "moe_shuffle_last_hip_error", "moe_shuffle_sum_expert_rows", "moe_shuffle_sum_rank_rows",
     "moe_shuffle_dispatch_backward", "moe_shuffle_combine_rank_partial", "moe_shuffle_combine_backward",
-    "moe_shuffle_dispatch_range", "moe_shuffle_combine_range",
+    "moe_shuffle_dispatch_range", "moe_shuffle_combine_range", "moe_shuffle_combine_rank_partial_f32",
 )
 
 
@@ -86,6 +86,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_shuffle_sum_rank_rows": (ctypes.c_int, [_vp, _vp, i64, _vp, _vp]),
         "moe_shuffle_dispatch_backward": (ctypes.c_int, [_vp, _vp, _vp, i64, _vp, _vp]),
         "moe_shuffle_combine_rank_partial": (ctypes.c_int, [_vp, _vp, _vp, _vp, i64, _vp, _vp]),
+        "moe_shuffle_combine_rank_partial_f32": (ctypes.c_int, [_vp, _vp, _vp, _vp, i64, _vp, _vp]),
         "moe_shuffle_combine_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
         "moe_shuffle_dispatch_range": (ctypes.c_int, [_vp, _vp, _vp, i64, _vp, ctypes.c_int32, ctypes.c_int32, _vp]),
         "moe_shuffle_combine_range": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp]),
@@ -204,6 +205,12 @@ def moe_shuffle_dispatch_backward(plan: Plan, grad_xe, grad_xr, grad_x, stream=N
 
 def moe_shuffle_combine_rank_partial(plan: Plan, ye, topk_w, partial, out, stream=None):
     _check("moe_shuffle_combine_rank_partial", load().moe_shuffle_combine_rank_partial(
+        plan.handle, _ptr(ye), _ptr(topk_w), _ptr(partial), partial.shape[0], _ptr(out), _stream(stream)))
+
+
+def moe_shuffle_combine_rank_partial_f32(plan: Plan, ye, topk_w, partial, out, stream=None):
+    """As moe_shuffle_combine_rank_partial with fp32 partial rows (partial: float32 [rows, H])."""
+    _check("moe_shuffle_combine_rank_partial_f32", load().moe_shuffle_combine_rank_partial_f32(
         plan.handle, _ptr(ye), _ptr(topk_w), _ptr(partial), partial.shape[0], _ptr(out), _stream(stream)))
 
 

@@ -342,6 +342,33 @@ int moe_shuffle_combine_rank_partial(moe_shuffle_plan_t plan, const void* ye, co
     return moe_shuffle_sum_rank_rows(plan, partial, partial_rows, out, stream);
 }
 
+int moe_shuffle_combine_rank_partial_f32(moe_shuffle_plan_t plan, const void* ye, const float* topk_w,
+                                         float* partial, int64_t partial_rows, void* out, void* stream)
+{
+    int rc = check_plan(plan);
+    if (rc) return rc;
+    const ms::Layout& L = plan->L;
+    if (L.T == 0) return MOE_SHUFFLE_OK;
+    if (!ye || !topk_w || !partial || !out) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (misaligned(ye, 16) || misaligned(partial, 16) || misaligned(out, 16) || misaligned(topk_w, 4))
+        return MOE_SHUFFLE_E_ALIGN;
+    const int64_t need = rank_rows_needed(plan);
+    if (partial_rows < need) return MOE_SHUFFLE_E_INVALID_ARG;
+    const size_t row = (size_t)L.H * 2, prow = (size_t)L.H * 4;
+    if (overlap(ye, row * (size_t)L.T * L.k, out, row * L.T) ||
+        overlap(ye, row * (size_t)L.T * L.k, partial, prow * (size_t)partial_rows) ||
+        overlap(partial, prow * (size_t)partial_rows, out, row * L.T))
+        return MOE_SHUFFLE_E_INVALID_ARG;
+    hipError_t e = ms::launch_sum_expert_rows(ye, (int64_t)L.T * L.k, topk_w, at<int32_t>(plan, L.comb_row),
+                                              at<float>(plan, L.gate_of_row), at<int32_t>(plan, L.fan_dst), L.D,
+                                              partial, need, at<int32_t>(plan, L.n_rank_rows), L.H,
+                                              at<int32_t>(plan, L.status), (hipStream_t)stream, true);
+    if (e != hipSuccess) return hip_fail(e);
+    e = ms::launch_sum_rank_rows(partial, partial_rows, at<int32_t>(plan, L.tok_rank_row), L.KR, out, L.T, L.H,
+                                 at<int32_t>(plan, L.status), (hipStream_t)stream, true);
+    return e == hipSuccess ? MOE_SHUFFLE_OK : hip_fail(e);
+}
+
 int moe_shuffle_combine_backward(moe_shuffle_plan_t plan, const void* grad_out, const void* ye, const float* topk_w,
                                  void* grad_ye, float* grad_w, void* stream)
 {

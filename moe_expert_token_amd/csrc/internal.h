@@ -60,13 +60,16 @@ hipError_t launch_combine_rows(const void* ye, const float* w, const int32_t* ro
 
 // out[p] = bf16( sum over q in fan_dst[p] of (gate(q) *) src[q] ) for p < n;
 // gate(q) is scattered from w through comb_row first when w is non-null.
+// With f32_out (w non-null only) out holds the fp32 sums, not rounded.
 hipError_t launch_sum_expert_rows(const void* src, int64_t src_rows, const float* w, const int32_t* comb_row,
                                   float* gate_of_row, const int32_t* fan_dst, int D, void* out, int64_t n_bound,
-                                  const int32_t* n_dev, int H, const int32_t* status, hipStream_t s);
+                                  const int32_t* n_dev, int H, const int32_t* status, hipStream_t s,
+                                  bool f32_out = false);
 
-// out[t] = bf16( sum over p in tok_rank_row[t] of src[p] ) for t < T.
+// out[t] = bf16( sum over p in tok_rank_row[t] of src[p] ) for t < T; with
+// f32_in the src rows are fp32.
 hipError_t launch_sum_rank_rows(const void* src, int64_t src_rows, const int32_t* tok_rank_row, int KR, void* out,
-                                int T, int H, const int32_t* status, hipStream_t s);
+                                int T, int H, const int32_t* status, hipStream_t s, bool f32_in = false);
 
 // The fan-out of the rank rows that belong to tokens [t0, t1) (t0, t1
 // multiples of kPlanTile, or t1 = T).

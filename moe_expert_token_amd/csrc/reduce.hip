@@ -24,11 +24,72 @@ namespace ms {
 enum WeightMode { kUnweighted = 0, kPerSlot = 1, kPerSourceRow = 2 };
 
 // One wave's unit: chunk c0 of output row `row`, its map row and gates in LDS.
-template <int U, bool FULL, int WMODE, bool NTL, bool NTS, int MAXW>
+// Row formats of a reduction: IO_BF16 bf16 rows in and out; IO_F32_OUT bf16
+// rows in, fp32 rows out (not rounded); IO_F32_IN fp32 rows in, bf16 out.
+// A wave's piece of a row is 64 element groups of 8 (one per lane): 1 KiB
+// of bf16, 2 KiB of fp32.  fp32 pieces move as two 1 KiB instructions, each
+// contiguous across the wave (lane l holds floats 4l .. 4l+3 of its half),
+// and are regrouped between lanes with shuffles, so that every memory
+// instruction covers whole cache lines.
+enum RowIO { IO_BF16 = 0, IO_F32_OUT = 1, IO_F32_IN = 2 };
+
+template <int IO>
+struct Term {
+    u32x4 a, b;  // fp32 pieces: the two contiguous 1 KiB halves as loaded
+};
+
+// The piece of a source row starting at element group cb; lanes past the
+// row's V groups load zeros.
+template <int IO, bool FULL, bool NTL>
+__device__ __forceinline__ Term<IO> load_term(const u32x4* row, int cb, int V, int lane)
+{
+    Term<IO> t;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    if constexpr (IO == IO_F32_IN) {
+        const int va = 2 * cb + lane, vb = 2 * cb + kWave + lane;  // 16-byte vectors of the fp32 row
+        t.a = (FULL || va < 2 * V) ? load_row16<NTL>(row + va) : zero;
+        t.b = (FULL || vb < 2 * V) ? load_row16<NTL>(row + vb) : zero;
+    } else {
+        t.a = (FULL || cb + lane < V) ? load_row16<NTL>(row + cb + lane) : zero;
+    }
+    return t;
+}
+
+// acc (this lane's 8 elements, group cb + lane) += wj * the term.  Called by
+// every lane of the wave (the fp32 form shuffles).
+template <int IO>
+__device__ __forceinline__ void fma_term(float acc[8], float wj, const Term<IO>& t, int lane)
+{
+    if constexpr (IO == IO_F32_IN) {
+        // group l sits in half A (l < 32) or B (l >= 32), lanes 2(l & 31) and 2(l & 31) + 1
+        const int src = 2 * (lane & (kWave / 2 - 1));
+        const bool in_b = lane >= kWave / 2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float lo_a = __shfl(__uint_as_float(t.a[e]), src, kWave);
+            const float lo_b = __shfl(__uint_as_float(t.b[e]), src, kWave);
+            const float hi_a = __shfl(__uint_as_float(t.a[e]), src + 1, kWave);
+            const float hi_b = __shfl(__uint_as_float(t.b[e]), src + 1, kWave);
+            acc[e] = __builtin_fmaf(wj, in_b ? lo_b : lo_a, acc[e]);
+            acc[4 + e] = __builtin_fmaf(wj, in_b ? hi_b : hi_a, acc[4 + e]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = __builtin_fmaf(wj, __uint_as_float(t.a[e] << 16), acc[2 * e]);
+            acc[2 * e + 1] = __builtin_fmaf(wj, __uint_as_float(t.a[e] & 0xffff0000u), acc[2 * e + 1]);
+        }
+    }
+}
+
+// One wave's unit: element groups c0 .. c0 + 64U - 1 of output row `row`
+// (lane l of piece i holds group c0 + 64i + l), its map row and gates in LDS.
+template <int U, bool FULL, int WMODE, bool NTL, bool NTS, int MAXW, int IO>
 __device__ __forceinline__ void reduce_unit_row(const u32x4* __restrict__ src, const int* trow, const int* tw,
                                                 int width, const float* __restrict__ w, u32x4* __restrict__ out,
                                                 int row, int c0, int V, int lane)
 {
+    const int src_stride = IO == IO_F32_IN ? 2 * V : V;  // 16-byte vectors per source row
     float acc[U][8];
 #pragma unroll
     for (int i = 0; i < U; ++i)
@@ -41,7 +102,8 @@ __device__ __forceinline__ void reduce_unit_row(const u32x4* __restrict__ src, c
     // which lets every load of the group be in flight at once.  Whole-row
     // units (U = 8) already carry 8 KiB per term and keep a plain loop: an
     // unrolled one hoists the next term's loads and the extra registers cost
-    // more occupancy than they buy.
+    // more occupancy than they buy.  Lanes past the row's end accumulate
+    // zeros and store nothing.
     constexpr int G = U >= 8 ? 1 : 8 / U;
     if constexpr (G == 1) {
 #pragma unroll 1
@@ -51,18 +113,10 @@ __device__ __forceinline__ void reduce_unit_row(const u32x4* __restrict__ src, c
             float wj = 1.0f;
             if (WMODE == kPerSlot) wj = __int_as_float(__builtin_amdgcn_readfirstlane(tw[j]));
             if (WMODE == kPerSourceRow) wj = w[q];
-            const u32x4* y = src + (int64_t)q * V + c0;
+            const u32x4* y = src + (int64_t)q * src_stride;
 #pragma unroll
             for (int i = 0; i < U; ++i) {
-                if (FULL || c0 + i * kWave + lane < V) {
-                    const u32x4 vv = load_row16<NTL>(y + i * kWave + lane);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        acc[i][2 * e] = __builtin_fmaf(wj, __uint_as_float(vv[e] << 16), acc[i][2 * e]);
-                        acc[i][2 * e + 1] =
-                            __builtin_fmaf(wj, __uint_as_float(vv[e] & 0xffff0000u), acc[i][2 * e + 1]);
-                    }
-                }
+                fma_term<IO>(acc[i], wj, load_term<IO, FULL, NTL>(y, c0 + i * kWave, V, lane), lane);
                 // one 1 KiB piece at a time keeps registers (and occupancy) at
                 // their best for whole-row units
                 __builtin_amdgcn_sched_barrier(0);
@@ -77,14 +131,13 @@ __device__ __forceinline__ void reduce_unit_row(const u32x4* __restrict__ src, c
 #pragma unroll
             for (int g = 0; g < G; ++g)
                 q[g] = (j0 + g < width) ? __builtin_amdgcn_readfirstlane(trow[j0 + g]) : -1;
-            u32x4 v[G][U];
+            Term<IO> v[G][U];
 #pragma unroll
             for (int g = 0; g < G; ++g)
                 if (q[g] >= 0) {
-                    const u32x4* y = src + (int64_t)q[g] * V + c0;
+                    const u32x4* y = src + (int64_t)q[g] * src_stride;
 #pragma unroll
-                    for (int i = 0; i < U; ++i)
-                        if (FULL || c0 + i * kWave + lane < V) v[g][i] = load_row16<NTL>(y + i * kWave + lane);
+                    for (int i = 0; i < U; ++i) v[g][i] = load_term<IO, FULL, NTL>(y, c0 + i * kWave, V, lane);
                 }
 #pragma unroll
             for (int g = 0; g < G; ++g) {
@@ -93,30 +146,42 @@ __device__ __forceinline__ void reduce_unit_row(const u32x4* __restrict__ src, c
                     if (WMODE == kPerSlot) wj = __int_as_float(__builtin_amdgcn_readfirstlane(tw[j0 + g]));
                     if (WMODE == kPerSourceRow) wj = w[q[g]];
 #pragma unroll
-                    for (int i = 0; i < U; ++i) {
-                        if (FULL || c0 + i * kWave + lane < V) {
-                            const u32x4 vv = v[g][i];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                acc[i][2 * e] = __builtin_fmaf(wj, __uint_as_float(vv[e] << 16), acc[i][2 * e]);
-                                acc[i][2 * e + 1] =
-                                    __builtin_fmaf(wj, __uint_as_float(vv[e] & 0xffff0000u), acc[i][2 * e + 1]);
-                            }
-                        }
-                    }
+                    for (int i = 0; i < U; ++i) fma_term<IO>(acc[i], wj, v[g][i], lane);
                 }
             }
             ended = q[G - 1] < 0;  // a -1 ends the map row; all later entries are -1 too
         }
     }
-    u32x4* o = out + (int64_t)row * V + c0;
+    if constexpr (IO == IO_F32_OUT) {
+        // lane l stores floats 4l .. 4l+3 of each contiguous 1 KiB half: half A
+        // holds groups c0 + 64i + (l >> 1), half B groups c0 + 64i + 32 + (l >> 1)
+        u32x4* o = out + (int64_t)row * (2 * V);
+        const int src_a = lane >> 1, src_b = kWave / 2 + (lane >> 1);
+        const bool upper = lane & 1;
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-        if (FULL || c0 + i * kWave + lane < V) {
-            u32x4 pk;
+        for (int i = 0; i < U; ++i) {
+            u32x4 pa, pb;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pk[e] = bf16_rne(acc[i][2 * e]) | (bf16_rne(acc[i][2 * e + 1]) << 16);
-            store_row16<NTS>(pk, o + i * kWave + lane);
+            for (int e = 0; e < 4; ++e) {
+                const float a_lo = __shfl(acc[i][e], src_a, kWave), a_hi = __shfl(acc[i][4 + e], src_a, kWave);
+                const float b_lo = __shfl(acc[i][e], src_b, kWave), b_hi = __shfl(acc[i][4 + e], src_b, kWave);
+                pa[e] = __float_as_uint(upper ? a_hi : a_lo);
+                pb[e] = __float_as_uint(upper ? b_hi : b_lo);
+            }
+            const int va = 2 * (c0 + i * kWave) + lane, vb = va + kWave;
+            if (FULL || va < 2 * V) store_row16<NTS>(pa, o + va);
+            if (FULL || vb < 2 * V) store_row16<NTS>(pb, o + vb);
+        }
+    } else {
+        u32x4* o = out + (int64_t)row * V + c0;
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            if (FULL || c0 + i * kWave + lane < V) {
+                u32x4 pk;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pk[e] = bf16_rne(acc[i][2 * e]) | (bf16_rne(acc[i][2 * e + 1]) << 16);
+                store_row16<NTS>(pk, o + i * kWave + lane);
+            }
         }
     }
 }
@@ -124,7 +189,7 @@ __device__ __forceinline__ void reduce_unit_row(const u32x4* __restrict__ src, c
 // Stages the map rows (and per-slot gates) of the block's units in LDS, then
 // one unit per wave.  With the row count on the device and L > 1, each
 // block takes L rounds of WPB units (as fanout_rows does).
-template <int U, bool FULL, int WMODE, bool NTL, bool NTS, int WPB, int MAXW, int L>
+template <int U, bool FULL, int WMODE, bool NTL, bool NTS, int WPB, int MAXW, int L, int IO>
 __device__ __forceinline__ void reduce_rows(int* s_tile, const u32x4* __restrict__ src,
                                             const int32_t* __restrict__ map, int width,
                                             const float* __restrict__ w, u32x4* __restrict__ out, int64_t n_bound,
@@ -153,14 +218,14 @@ __device__ __forceinline__ void reduce_rows(int* s_tile, const u32x4* __restrict
         const int u = u0 + wave;
         const int row = fdiv(u, rs.div);
         if (row < n)
-            reduce_unit_row<U, FULL, WMODE, NTL, NTS, MAXW>(src, s_rows + (row - first) * width,
+            reduce_unit_row<U, FULL, WMODE, NTL, NTS, MAXW, IO>(src, s_rows + (row - first) * width,
                                                             s_w + (row - first) * width, width, w, out, row,
                                                             (u - row * rs.cpr) * (kWave * U), rs.V, lane);
     }
 }
 
 #define MS_REDUCE_KERNEL(NAME, NTL, NTS)                                                                         \
-    template <int U, bool FULL, int WMODE, int WPB, int MAXW, int L>                                             \
+    template <int U, bool FULL, int WMODE, int WPB, int MAXW, int L, int IO>                                     \
     __global__ __launch_bounds__(WPB * kWave) void NAME(const u32x4* __restrict__ src,                           \
                                                         const int32_t* __restrict__ map, int width,             \
                                                         const float* __restrict__ w, u32x4* __restrict__ out,   \
@@ -168,8 +233,8 @@ __device__ __forceinline__ void reduce_rows(int* s_tile, const u32x4* __restrict
                                                         RowSplit rs, const int32_t* __restrict__ status)        \
     {                                                                                                            \
         extern __shared__ int s_tile[];                                                                          \
-        reduce_rows<U, FULL, WMODE, NTL, NTS, WPB, MAXW, L>(s_tile, src, map, width, w, out, n_bound, n_dev, rs, \
-                                                            status);                                             \
+        reduce_rows<U, FULL, WMODE, NTL, NTS, WPB, MAXW, L, IO>(s_tile, src, map, width, w, out, n_bound, n_dev, \
+                                                                rs, status);                                     \
     }
 // ye (expert-major) -> out (token-major): the forward combine.
 MS_REDUCE_KERNEL(combine_rows_kernel, MS_COMBINE_NT_LOAD, MS_COMBINE_NT_STORE)
@@ -223,31 +288,31 @@ enum ReduceKind { kCombine = 0, kSumExpertRows = 1, kSumRankRows = 2 };
 #define MS_SUMX_ROUNDS 1
 #endif
 
-template <int KIND, int U, bool FULL, int WMODE, int WPB, int MAXW, int L>
+template <int KIND, int U, bool FULL, int WMODE, int WPB, int MAXW, int L, int IO>
 static void launch_reduce_kernel(dim3 grid, size_t lds, hipStream_t s, const u32x4* src, const int32_t* map,
                                  int width, const float* w, u32x4* out, int64_t n_bound, const int32_t* n_dev,
                                  RowSplit rs, const int32_t* status)
 {
     const dim3 block(WPB * kWave);
     if constexpr (KIND == kCombine)
-        hipLaunchKernelGGL((combine_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1>), grid, block, lds, s, src, map, width,
-                           w, out, n_bound, n_dev, rs, status);
+        hipLaunchKernelGGL((combine_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1, IO_BF16>), grid, block, lds, s, src, map,
+                           width, w, out, n_bound, n_dev, rs, status);
     else if constexpr (KIND == kSumExpertRows && L > 1) {
         if (n_dev)
-            hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW, L>), grid, block, lds, s, src, map,
-                               width, w, out, n_bound, n_dev, rs, status);
+            hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW, L, IO>), grid, block, lds, s, src,
+                               map, width, w, out, n_bound, n_dev, rs, status);
         else
-            hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1>), grid, block, lds, s, src, map,
-                               width, w, out, n_bound, n_dev, rs, status);
+            hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1, IO>), grid, block, lds, s, src,
+                               map, width, w, out, n_bound, n_dev, rs, status);
     } else if constexpr (KIND == kSumExpertRows)
-        hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1>), grid, block, lds, s, src, map,
+        hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1, IO>), grid, block, lds, s, src, map,
                            width, w, out, n_bound, n_dev, rs, status);
     else
-        hipLaunchKernelGGL((sum_rank_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1>), grid, block, lds, s, src, map, width,
-                           w, out, n_bound, n_dev, rs, status);
+        hipLaunchKernelGGL((sum_rank_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1, IO>), grid, block, lds, s, src, map,
+                           width, w, out, n_bound, n_dev, rs, status);
 }
 
-template <int KIND, int WMODE, int U, int WPB>
+template <int KIND, int WMODE, int U, int WPB, int IO>
 static hipError_t launch_reduce_uw(const void* src, const int32_t* map, int width, const float* w, void* out,
                                    int64_t n_bound, const int32_t* n_dev, int V, const int32_t* status, hipStream_t s)
 {
@@ -263,43 +328,45 @@ static hipError_t launch_reduce_uw(const void* src, const int32_t* map, int widt
     u32x4* op = (u32x4*)out;
     const bool full = V % (kWave * U) == 0;
     if (width <= 8 && full)
-        launch_reduce_kernel<KIND, U, true, WMODE, WPB, 8, L>(grid, lds, s, sp, map, width, w, op, n_bound, n_dev, rs,
-                                                           status);
+        launch_reduce_kernel<KIND, U, true, WMODE, WPB, 8, L, IO>(grid, lds, s, sp, map, width, w, op, n_bound, n_dev,
+                                                                  rs, status);
     else if (width <= 8)
-        launch_reduce_kernel<KIND, U, false, WMODE, WPB, 8, L>(grid, lds, s, sp, map, width, w, op, n_bound, n_dev, rs,
-                                                            status);
-    else if (full)
-        launch_reduce_kernel<KIND, U, true, WMODE, WPB, kMaxTopK, L>(grid, lds, s, sp, map, width, w, op, n_bound,
-                                                                  n_dev, rs, status);
-    else
-        launch_reduce_kernel<KIND, U, false, WMODE, WPB, kMaxTopK, L>(grid, lds, s, sp, map, width, w, op, n_bound,
+        launch_reduce_kernel<KIND, U, false, WMODE, WPB, 8, L, IO>(grid, lds, s, sp, map, width, w, op, n_bound,
                                                                    n_dev, rs, status);
+    else if (full)
+        launch_reduce_kernel<KIND, U, true, WMODE, WPB, kMaxTopK, L, IO>(grid, lds, s, sp, map, width, w, op, n_bound,
+                                                                         n_dev, rs, status);
+    else
+        launch_reduce_kernel<KIND, U, false, WMODE, WPB, kMaxTopK, L, IO>(grid, lds, s, sp, map, width, w, op,
+                                                                          n_bound, n_dev, rs, status);
     return hipGetLastError();
 }
 
-template <int KIND, int WMODE, int U>
+template <int KIND, int WMODE, int U, int IO>
 static hipError_t launch_reduce_u(const void* src, const int32_t* map, int width, const float* w, void* out,
                                   int64_t n_bound, const int32_t* n_dev, int V, const int32_t* status, hipStream_t s)
 {
     if constexpr (U <= 2) {
         if (n_dev)
-            return launch_reduce_uw<KIND, WMODE, U, kWavesBig>(src, map, width, w, out, n_bound, n_dev, V, status, s);
+            return launch_reduce_uw<KIND, WMODE, U, kWavesBig, IO>(src, map, width, w, out, n_bound, n_dev, V, status,
+                                                                   s);
     }
-    return launch_reduce_uw<KIND, WMODE, U, kWavesPerBlock>(src, map, width, w, out, n_bound, n_dev, V, status, s);
+    return launch_reduce_uw<KIND, WMODE, U, kWavesPerBlock, IO>(src, map, width, w, out, n_bound, n_dev, V, status, s);
 }
 
-template <int KIND, int WMODE>
+template <int KIND, int WMODE, int IO = IO_BF16>
 static hipError_t launch_reduce(const void* src, int64_t src_rows, const int32_t* map, int width, const float* w,
                                 void* out, int64_t n_bound, const int32_t* n_dev, int H, const int32_t* status,
                                 hipStream_t s)
 {
     if (n_bound <= 0) return hipSuccess;
     const int V = H / 8;
-    switch (reduce_unit(KIND, V, src_rows * (int64_t)H * 2)) {
-        case 1: return launch_reduce_u<KIND, WMODE, 1>(src, map, width, w, out, n_bound, n_dev, V, status, s);
-        case 2: return launch_reduce_u<KIND, WMODE, 2>(src, map, width, w, out, n_bound, n_dev, V, status, s);
-        case 4: return launch_reduce_u<KIND, WMODE, 4>(src, map, width, w, out, n_bound, n_dev, V, status, s);
-        default: return launch_reduce_u<KIND, WMODE, 8>(src, map, width, w, out, n_bound, n_dev, V, status, s);
+    const int64_t src_bytes = src_rows * (int64_t)H * (IO == IO_F32_IN ? 4 : 2);
+    switch (reduce_unit(KIND, V, src_bytes)) {
+        case 1: return launch_reduce_u<KIND, WMODE, 1, IO>(src, map, width, w, out, n_bound, n_dev, V, status, s);
+        case 2: return launch_reduce_u<KIND, WMODE, 2, IO>(src, map, width, w, out, n_bound, n_dev, V, status, s);
+        case 4: return launch_reduce_u<KIND, WMODE, 4, IO>(src, map, width, w, out, n_bound, n_dev, V, status, s);
+        default: return launch_reduce_u<KIND, WMODE, 8, IO>(src, map, width, w, out, n_bound, n_dev, V, status, s);
     }
 }
 
@@ -322,22 +389,30 @@ __global__ __launch_bounds__(kBlock) void gate_of_row_kernel(const float* __rest
 
 hipError_t launch_sum_expert_rows(const void* src, int64_t src_rows, const float* w, const int32_t* comb_row,
                                   float* gate_of_row, const int32_t* fan_dst, int D, void* out, int64_t n_bound,
-                                  const int32_t* n_dev, int H, const int32_t* status, hipStream_t s)
+                                  const int32_t* n_dev, int H, const int32_t* status, hipStream_t s, bool f32_out)
 {
     if (n_bound <= 0) return hipSuccess;
-    if (!w) return launch_reduce<kSumExpertRows, kUnweighted>(src, src_rows, fan_dst, D, nullptr, out, n_bound,
-                                                              n_dev, H, status, s);
+    if (!w && !f32_out)
+        return launch_reduce<kSumExpertRows, kUnweighted>(src, src_rows, fan_dst, D, nullptr, out, n_bound, n_dev, H,
+                                                          status, s);
+    if (!w) return hipErrorInvalidValue;  // fp32 partials are only made for the weighted return path
     hipLaunchKernelGGL(gate_of_row_kernel, dim3((unsigned)((src_rows + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, w,
                        comb_row, src_rows, gate_of_row, status);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (f32_out)
+        return launch_reduce<kSumExpertRows, kPerSourceRow, IO_F32_OUT>(src, src_rows, fan_dst, D, gate_of_row, out,
+                                                                        n_bound, n_dev, H, status, s);
     return launch_reduce<kSumExpertRows, kPerSourceRow>(src, src_rows, fan_dst, D, gate_of_row, out, n_bound, n_dev,
                                                         H, status, s);
 }
 
 hipError_t launch_sum_rank_rows(const void* src, int64_t src_rows, const int32_t* tok_rank_row, int KR, void* out,
-                                int T, int H, const int32_t* status, hipStream_t s)
+                                int T, int H, const int32_t* status, hipStream_t s, bool f32_in)
 {
+    if (f32_in)
+        return launch_reduce<kSumRankRows, kUnweighted, IO_F32_IN>(src, src_rows, tok_rank_row, KR, nullptr, out, T,
+                                                                   nullptr, H, status, s);
     return launch_reduce<kSumRankRows, kUnweighted>(src, src_rows, tok_rank_row, KR, nullptr, out, T, nullptr, H,
                                                     status, s);
 }

@@ -138,6 +138,9 @@ def check_backward_case(idx, w, H, E, R, ye, grad_xe, grad_out, name=""):
     gw = torch.full((max(T * k, 1),), float("nan"), dtype=torch.float32, device="cuda")
     ms.moe_shuffle_dispatch_backward(plan, gxe_d, gxr, gx)
     ms.moe_shuffle_combine_rank_partial(plan, ye_d, w_d, part, out)
+    part32 = torch.full((rows, H), float("nan"), dtype=torch.float32, device="cuda")
+    out32 = full(T)
+    ms.moe_shuffle_combine_rank_partial_f32(plan, ye_d, w_d, part32, out32)
     ms.moe_shuffle_combine_backward(plan, gout_d, ye_d, w_d, gye, gw)
     info = ms.moe_shuffle_plan_query(plan)
     torch.cuda.synchronize()
@@ -151,6 +154,10 @@ def check_backward_case(idx, w, H, E, R, ye, grad_xe, grad_out, name=""):
     o_part, o_out = orc.combine_rank_partial(o, ye, w, E, R)
     np.testing.assert_array_equal(to_host16(part)[:N], o_part, err_msg="partial")
     np.testing.assert_array_equal(to_host16(out)[:T], o_out, err_msg="rank-partial out")
+    o_part32, o_out32 = orc.combine_rank_partial_f32(o, ye, w, E, R)
+    np.testing.assert_array_equal(part32.cpu().numpy()[:N].view(np.uint32), o_part32.view(np.uint32),
+                                  err_msg="fp32 partial")
+    np.testing.assert_array_equal(to_host16(out32)[:T], o_out32, err_msg="fp32-partial out")
     o_gye, o_gw = orc.combine_backward(o["comb_row"], grad_out, ye, w, E, R)
     np.testing.assert_array_equal(to_host16(gye)[:T * k], o_gye, err_msg="grad_ye")
     if T:

@@ -47,8 +47,8 @@ __device__ __forceinline__ float reduce_scatter8(const float p[8], int lane)
 // partials.  Two passes, a write-heavy one (read grad_out, write k rows)
 // and a read-only one (read grad_out and k rows), against one pass doing
 // both, whose mix of k row reads and k row writes per token keeps HBM from
-// streaming: 1717 us against 1841 us (long prefill), 775 against 792 us
-// (skewed), 436 us either way (DeepSeek-V3-like), on the MI355X.
+// streaming: backward step 3.655 ms against 3.815 ms (one pass, U = 2; long
+// prefill) and 0.831 against 0.841 ms (DeepSeek-V3-like) on the MI355X.
 template <int U, bool FULL, int PART>
 __device__ __forceinline__ void combine_bwd_rows(int* s_tile, const u32x4* __restrict__ grad_out,
                                                  const u32x4* __restrict__ ye, const float* __restrict__ w,
@@ -179,16 +179,17 @@ __global__ __launch_bounds__(kBlock) void gate_grad_kernel(const float* __restri
 
 // Vectors per lane of a unit in the two passes, chosen on whole backward
 // steps on the MI355X: grad_ye at U = 1 with the partials at U = 2 ran
-// 1.444 ms (skewed) and 3.840 ms (long prefill) against 1.472 and 3.898 ms
-// with U = 2 for both, and 1.48 and 3.96 ms for one fused pass at U = 1.
+// 3.633 ms (long prefill) against 3.690 ms with the partials at U = 1 and
+// 3.723 ms with grad_ye at U = 2.
 #ifndef MS_CBWD_GRAD_UNIT
 #define MS_CBWD_GRAD_UNIT 1
 #endif
 #ifndef MS_CBWD_DOT_UNIT
 #define MS_CBWD_DOT_UNIT 2
 #endif
-// Pass order: grad_ye first.  The partials first measured 0.900 against
-// 0.878 ms per backward step (DeepSeek-V3-like).
+// Pass order: grad_ye first.  With plain loads the partials first measured
+// 0.900 against 0.878 ms per backward step (DeepSeek-V3-like); with
+// non-temporal loads the order makes no difference (0.833 against 0.831).
 #ifndef MS_CBWD_DOT_FIRST
 #define MS_CBWD_DOT_FIRST 0
 #endif

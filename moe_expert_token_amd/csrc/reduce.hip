@@ -272,8 +272,24 @@ MS_REDUCE_KERNEL(sum_rank_rows_kernel, MS_SUMR_NT_LOAD, MS_SUMR_NT_STORE)
 #define MS_SUMR_UNIT_LARGE MS_COMBINE_UNIT_LARGE
 #endif
 
-static int reduce_unit(int kind, int V, int64_t src_bytes)
+// fp32 partial rows: the receiver's sum that writes them takes 1 KiB units
+// and the sender's sum that reads them 2 KiB units (4 KiB of fp32 per
+// term).  Where a token reaches about 4 ranks, a group of 8 slots at U = 1
+// holds about 4 live terms; at U = 2 all of them go out in one group of 4
+// with twice the bytes each, so a wave keeps twice the loads in flight.
+// Measured per rank-partial combine with fp32 partials: skewed 1.169 ->
+// 1.024 ms, long prefill 3.406 -> 3.192 ms.
+#ifndef MS_SUMX_F32_UNIT
+#define MS_SUMX_F32_UNIT 1
+#endif
+#ifndef MS_SUMR_F32_UNIT
+#define MS_SUMR_F32_UNIT 2
+#endif
+
+static int reduce_unit(int kind, int io, int V, int64_t src_bytes)
 {
+    if (io == IO_F32_OUT) return fit_unit(V, MS_SUMX_F32_UNIT);
+    if (io == IO_F32_IN) return fit_unit(V, MS_SUMR_F32_UNIT);
     const bool large = src_bytes > (int64_t)MS_COMBINE_LARGE_BYTES;
     const int small_unit = kind == 1 ? MS_SUMX_UNIT : kind == 2 ? MS_SUMR_UNIT : MS_COMBINE_UNIT;
     const int large_unit = kind == 1 ? MS_SUMX_UNIT_LARGE : kind == 2 ? MS_SUMR_UNIT_LARGE : MS_COMBINE_UNIT_LARGE;
@@ -362,7 +378,7 @@ static hipError_t launch_reduce(const void* src, int64_t src_rows, const int32_t
     if (n_bound <= 0) return hipSuccess;
     const int V = H / 8;
     const int64_t src_bytes = src_rows * (int64_t)H * (IO == IO_F32_IN ? 4 : 2);
-    switch (reduce_unit(KIND, V, src_bytes)) {
+    switch (reduce_unit(KIND, IO, V, src_bytes)) {
         case 1: return launch_reduce_u<KIND, WMODE, 1, IO>(src, map, width, w, out, n_bound, n_dev, V, status, s);
         case 2: return launch_reduce_u<KIND, WMODE, 2, IO>(src, map, width, w, out, n_bound, n_dev, V, status, s);
         case 4: return launch_reduce_u<KIND, WMODE, 4, IO>(src, map, width, w, out, n_bound, n_dev, V, status, s);

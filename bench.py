@@ -89,6 +89,30 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def copy_bytes_of(T, H, k):
+    """Size of the reference copy: a buffer as large as xe, at most 2 GiB."""
+    return min(T * k * H * 2, 2 << 30)
+
+
+def copy_reference(dev, T, H, k):
+    """The runtime's device-to-device copy of copy_bytes_of(T, H, k) bytes
+    (read + write GB/s).  It is also the kernel of known size that scales the
+    FETCH_SIZE / WRITE_SIZE counters of a --pmc run."""
+    import torch
+    nbytes = copy_bytes_of(T, H, k)
+    a = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        b.copy_(a)
+    c1.record()
+    torch.cuda.synchronize()
+    return 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+
 def n_rank_rows(topk_idx, E, R):
     """Distinct (token, rank) pairs of a routing (bookkeeping for byte counts)."""
     import numpy as np
@@ -112,7 +136,7 @@ def pmc_summary(args):
     idx, _ = synth.make_routing(cfg, args.seed)
     N = n_rank_rows(idx, E, R)
     B = algorithmic_bytes(T, H, k, N)
-    copy_bytes = min(T * k * H * 2, 2 << 30)
+    copy_bytes = copy_bytes_of(T, H, k)
 
     def per_kernel(path):
         vals = collections.defaultdict(list)
@@ -139,6 +163,8 @@ def pmc_summary(args):
     f_factor = copy_bytes / (max(fetch[copy_name]) * 1024)
     w_factor = copy_bytes / (max(write[copy_name]) * 1024)
     stats = {r["Name"]: r for r in csv.DictReader(open(args.trace_stats))}
+    if args.path != "forward":
+        return pmc_path_summary(args, cfg, N, fetch, write, f_factor, w_factor, stats, copy_bytes)
 
     short = {"dispatch_send_kernel": "send", "dispatch_fanout_kernel": "fanout", "combine_rows_kernel": "combine"}
     digest = args.src_sha or source_digest()
@@ -181,6 +207,58 @@ def pmc_summary(args):
         lines.append(f"| `{n.split('(')[0]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
     with open(os.path.join(args.out_dir, f"kernels_{cfg.name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# The kernels that make up each call of the other paths (by kernel name).
+PATH_KERNELS = {
+    "backward": {"combine_bwd": ("combine_bwd_grad_kernel", "combine_bwd_dot_kernel", "gate_grad_kernel"),
+                 "sum_expert_rows": ("sum_expert_rows_kernel",), "sum_rank_rows": ("sum_rank_rows_kernel",)},
+    "rank-partial": {"sum_expert_rows": ("gate_of_row_kernel", "sum_expert_rows_kernel"),
+                     "sum_rank_rows": ("sum_rank_rows_kernel",)},
+}
+PATH_KERNELS["rank-partial-f32"] = PATH_KERNELS["rank-partial"]
+
+
+def pmc_path_summary(args, cfg, N, fetch, write, f_factor, w_factor, stats, copy_bytes):
+    """The counter summary of --path backward / rank-partial / rank-partial-f32:
+    HBM bytes per launch of every kernel and, per call of the path, the sum
+    over its kernels against the call's algorithmic bytes."""
+    T, H, k = cfg.T, cfg.H, cfg.k
+    B = path_bytes(args.path, T, H, k, N)
+    digest = args.src_sha or source_digest()
+    mean = lambda v: sum(v) / len(v)  # noqa: E731
+    per = {}
+    for name in set(fetch) & set(write):
+        if "copyBuffer" in name:
+            continue
+        base = name.split("(")[0].replace("void ", "").split("<")[0].replace("ms::", "")
+        st = next((r for n, r in stats.items() if n.split("(")[0] == name.split("(")[0]), None)
+        per[name.split("(")[0]] = (base, float(st["AverageNs"]) / 1e3 if st else float("nan"),
+                                   mean(fetch[name]) * 1024 * f_factor, mean(write[name]) * 1024 * w_factor)
+    lines = [f"# Kernel time and HBM traffic — {cfg.name}, path {args.path}", "",
+             f"T={T} H={H} E={cfg.E} k={k} R={cfg.R}, N={N}; kernel source sha256[:16] {digest}.", "",
+             "Commands (run from the repository root on one MI355X):", ""]
+    lines += [f"    {c}" for c in args.commands] + [""]
+    lines += [f"Counter scale from the runtime copy kernel of {copy_bytes} bytes in the same runs: "
+              f"FETCH_SIZE x {f_factor:.4f}, WRITE_SIZE x {w_factor:.4f}.", "",
+              "| call | kernels | avg us (trace, sum) | HBM read MB | HBM write MB | algorithmic MB | traffic / alg |",
+              "|---|---|---|---|---|---|---|"]
+    for call, kernels in PATH_KERNELS[args.path].items():
+        mine = [v for v in per.values() if v[0] in kernels]
+        us, fb, wb = sum(v[1] for v in mine), sum(v[2] for v in mine), sum(v[3] for v in mine)
+        lines.append(f"| {call} | {', '.join(sorted(v[0] for v in mine))} | {us:.1f} | {fb / 1e6:.1f} | "
+                     f"{wb / 1e6:.1f} | {B[call] / 1e6:.1f} | {(fb + wb) / B[call]:.3f} |")
+    lines += ["", "| kernel | avg us (trace) | HBM read MB | HBM write MB |", "|---|---|---|---|"]
+    for full, (base, us, fb, wb) in sorted(per.items(), key=lambda kv: -kv[1][1] if kv[1][1] == kv[1][1] else 0):
+        lines.append(f"| `{full}` | {us:.1f} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
+    lines += ["", "Kernel trace summary (rocprofv3 --stats):", "", "| kernel | calls | avg us | min us | max us |",
+              "|---|---|---|---|---|"]
+    for n, r in stats.items():
+        lines.append(f"| `{n.split('(')[0]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    with open(os.path.join(args.out_dir, f"kernels_{args.path}_{cfg.name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -275,6 +353,7 @@ def bench_path(args):
     us = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]) * 1e3)
           for j, n in enumerate(names)}
     B = path_bytes(args.path, T, H, k, N)
+    copy_gbps = copy_reference(dev, T, H, k)
     parity = None
     if not args.no_parity:
         import oracle
@@ -312,6 +391,7 @@ def bench_path(args):
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(B[dom] / (us[dom] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4), "traffic": None,
                      "alg_bytes_per_launch": B[dom], "avg_launch_us": round(us[dom], 2)},
+        "copy_ceiling_GBps": round(copy_gbps, 1),
         "cpu_baseline": None, "parity": parity, "kernel_src_sha256_16": source_digest(),
     }
     ms.moe_shuffle_plan_destroy(plan)
@@ -541,20 +621,7 @@ def main():
     B = algorithmic_bytes(T, H, k, N)
     log(f"[bench] {ms_per_step:.3f} ms/step; kernels (us): " + ", ".join(f"{n} {us[n]:.1f}" for n in names))
 
-    # copy ceiling: the runtime's device-to-device copy of a buffer as big as xe
-    nbytes = min(T * k * H * 2, 2 << 30)
-    a = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
-    b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(10):
-        b.copy_(a)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_gbps = 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del a, b
+    copy_gbps = copy_reference(dev, T, H, k)
 
     parity = None
     if not args.no_parity:

@@ -68,6 +68,51 @@ def test_counter_summary_scales_by_the_copy_kernel(tmp_path):
     assert (out / f"kernels_{cfg.name}.md").exists()
 
 
+def test_path_counter_summary_sums_the_kernels_of_each_call(tmp_path):
+    """--path backward: the three kernels of the combine backward count as
+    one call; counters equal to the algorithmic bytes give a ratio of 1."""
+    cfg = synth.CONFIGS[0]
+    copy_bytes = bench.copy_bytes_of(cfg.T, cfg.H, cfg.k)
+    idx, _ = synth.make_routing(cfg, 0)
+    N = bench.n_rank_rows(idx, cfg.E, cfg.R)
+    B = bench.path_bytes("backward", cfg.T, cfg.H, cfg.k, N)
+    sig = "(unsigned int __vector(4) const*, int)"
+    # the combine backward's bytes split over its three kernels, all reads (FETCH_SIZE scale 2)
+    parts = {"void ms::combine_bwd_grad_kernel<1, true>": B["combine_bwd"] * 0.5,
+             "void ms::combine_bwd_dot_kernel<2, true>": B["combine_bwd"] * 0.25,
+             "ms::gate_grad_kernel": B["combine_bwd"] * 0.25,
+             "void ms::sum_expert_rows_kernel<2, true, 0, 4, 8, 1, 0>": B["sum_expert_rows"],
+             "void ms::sum_rank_rows_kernel<1, true, 0, 4, 8, 1, 0>": B["sum_rank_rows"]}
+    fetch = [(COPY, "FETCH_SIZE", copy_bytes / 2 / 1024)]
+    write = [(COPY, "WRITE_SIZE", copy_bytes / 1024)]
+    for name, b in parts.items():
+        for _ in range(3):  # three launches of each, same counts
+            fetch.append((name + sig, "FETCH_SIZE", b / 2 / 1024))
+            write.append((name + sig, "WRITE_SIZE", 0.0))
+    _counter_csv(tmp_path / "fetch.csv", fetch)
+    _counter_csv(tmp_path / "write.csv", write)
+    with open(tmp_path / "stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        for name in parts:
+            w.writerow([name + sig, 3, 3000, 1000.0, 20, 900, 1100, 0])
+    out = tmp_path / "out"
+    out.mkdir()
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--pmc-summary", "--path", "backward",
+                        "--config", "0", "--src-sha", "0123456789abcdef", "--fetch-csv", str(tmp_path / "fetch.csv"),
+                        "--write-csv", str(tmp_path / "write.csv"), "--trace-stats", str(tmp_path / "stats.csv"),
+                        "--out-dir", str(out)], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    text = open(out / f"kernels_backward_{cfg.name}.md").read()
+    calls = {ln.split("|")[1].strip(): ln.split("|") for ln in text.splitlines()
+             if ln.startswith("| combine_bwd") or ln.startswith("| sum_")}
+    assert set(calls) == {"combine_bwd", "sum_expert_rows", "sum_rank_rows"}
+    assert calls["combine_bwd"][2].strip() == "combine_bwd_dot_kernel, combine_bwd_grad_kernel, gate_grad_kernel"
+    assert float(calls["combine_bwd"][3]) == pytest.approx(3.0)  # three kernels of 1 us each
+    for c in calls.values():
+        assert c[7].strip() == "1.000"
+
+
 def test_stored_traffic_is_used_only_for_the_profiled_source(tmp_path, monkeypatch):
     (tmp_path / "profiles").mkdir()
     path = tmp_path / "profiles" / "traffic_dispatch_fanout_kernel_w.json"

@@ -264,6 +264,19 @@ int moe_shuffle_plan_query(moe_shuffle_plan_t plan, void* stream, moe_shuffle_pl
 /* Device pointers of the plan arrays (no device work, no sync). */
 int moe_shuffle_plan_arrays_get(moe_shuffle_plan_t plan, moe_shuffle_plan_arrays* arrays);
 
+/* ---- measurement helper (not a step of the shuffle) ----
+ * The reference streaming copy: dst[0 .. bytes) = src[0 .. bytes), 16-byte
+ * vectors with the non-temporal hint, one per lane.  It gives the HBM
+ * ceiling of a plain copy on the device at hand, against which the row
+ * kernels' bandwidth is read.
+ *   src, dst  device, 16 B aligned, not overlapping; caller-owned
+ *   bytes     a multiple of 16 (0 launches nothing)
+ * Returns MOE_SHUFFLE_E_ALIGN for a misaligned pointer or size,
+ * MOE_SHUFFLE_E_INVALID_ARG for NULL or overlapping buffers,
+ * MOE_SHUFFLE_E_OVERFLOW past 2^31 - 1 blocks of 4 KiB.  Asynchronous on
+ * `stream`. */
+int moe_shuffle_copy_reference(const void* src, void* dst, size_t bytes, void* stream);
+
 /* Frees the host handle (not the workspace).  NULL is ignored. */
 void moe_shuffle_plan_destroy(moe_shuffle_plan_t plan);
 

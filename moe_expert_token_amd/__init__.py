@@ -12,5 +12,5 @@ from ._lib import (  # noqa: F401
     moe_shuffle_plan_destroy, moe_shuffle_plan_query, moe_shuffle_strerror, moe_shuffle_workspace_size,
     plan_array_views, moe_shuffle_sum_expert_rows, moe_shuffle_sum_rank_rows, moe_shuffle_dispatch_backward,
     moe_shuffle_combine_rank_partial, moe_shuffle_combine_backward, moe_shuffle_dispatch_range,
-    moe_shuffle_combine_range, moe_shuffle_combine_rank_partial_f32,
+    moe_shuffle_combine_range, moe_shuffle_combine_rank_partial_f32, moe_shuffle_copy_reference,
 )

@@ -26,6 +26,7 @@ EXPORTS = (
     "moe_shuffle_last_hip_error", "moe_shuffle_sum_expert_rows", "moe_shuffle_sum_rank_rows",
     "moe_shuffle_dispatch_backward", "moe_shuffle_combine_rank_partial", "moe_shuffle_combine_backward",
     "moe_shuffle_dispatch_range", "moe_shuffle_combine_range", "moe_shuffle_combine_rank_partial_f32",
+    "moe_shuffle_copy_reference",
 )
 
 
@@ -90,6 +91,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_shuffle_combine_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
         "moe_shuffle_dispatch_range": (ctypes.c_int, [_vp, _vp, _vp, i64, _vp, ctypes.c_int32, ctypes.c_int32, _vp]),
         "moe_shuffle_combine_range": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp]),
+        "moe_shuffle_copy_reference": (ctypes.c_int, [_vp, _vp, ctypes.c_size_t, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -186,6 +188,15 @@ def moe_shuffle_dispatch_fanout(plan: Plan, xr, xe, stream=None):
 def moe_shuffle_combine(plan: Plan, ye, topk_w, out, stream=None):
     _check("moe_shuffle_combine", load().moe_shuffle_combine(plan.handle, _ptr(ye), _ptr(topk_w), _ptr(out),
                                                              _stream(stream)))
+
+
+def moe_shuffle_copy_reference(src, dst, nbytes=None, stream=None):
+    """The reference streaming copy (a bandwidth yardstick, not a step of the
+    shuffle): the first nbytes (default: all of src) of src into dst."""
+    if nbytes is None:
+        nbytes = src.numel() * src.element_size()
+    _check("moe_shuffle_copy_reference", load().moe_shuffle_copy_reference(_ptr(src), _ptr(dst), int(nbytes),
+                                                                           _stream(stream)))
 
 
 def moe_shuffle_sum_expert_rows(plan: Plan, expert_rows, topk_w, rank_rows, stream=None):

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_shuffle.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("abi.hip", "plan.hip", "rows.hip", "reduce.hip", "combine_bwd.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("abi.hip", "plan.hip", "rows.hip", "reduce.hip", "combine_bwd.hip", "copy_ref.hip")]
 ARCH = os.environ.get("MOE_SHUFFLE_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

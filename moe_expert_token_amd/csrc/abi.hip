@@ -481,6 +481,17 @@ int moe_shuffle_plan_arrays_get(moe_shuffle_plan_t plan, moe_shuffle_plan_arrays
     return MOE_SHUFFLE_OK;
 }
 
+int moe_shuffle_copy_reference(const void* src, void* dst, size_t bytes, void* stream)
+{
+    if (bytes == 0) return MOE_SHUFFLE_OK;
+    if (!src || !dst) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (bytes % 16 || misaligned(src, 16) || misaligned(dst, 16)) return MOE_SHUFFLE_E_ALIGN;
+    if (overlap(src, bytes, dst, bytes)) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (bytes / 16 > (size_t)0x7fffffff * ms::kBlock) return MOE_SHUFFLE_E_OVERFLOW;
+    const hipError_t e = ms::launch_copy_reference(src, dst, (int64_t)(bytes / 16), (hipStream_t)stream);
+    return e == hipSuccess ? MOE_SHUFFLE_OK : hip_fail(e);
+}
+
 void moe_shuffle_plan_destroy(moe_shuffle_plan_t plan) { free(plan); }
 
 const char* moe_shuffle_strerror(int code)

@@ -82,4 +82,7 @@ hipError_t launch_combine_backward(const void* grad_out, const void* ye, const f
                                    void* grad_ye, float* grad_w, float* dots, int T, int k, int H,
                                    const int32_t* status, hipStream_t s);
 
+// dst[i] = src[i] for the n_vectors 16-byte vectors (the reference copy).
+hipError_t launch_copy_reference(const void* src, void* dst, int64_t n_vectors, hipStream_t s);
+
 }  // namespace ms

@@ -2,6 +2,7 @@
  * checks that the header is plain C and that the host-only entry points
  * (no device work) behave as declared.  Prints one line per check and
  * exits non-zero on the first failure. */
+#include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -36,6 +37,14 @@ int main(void)
     moe_shuffle_plan_arrays arrays;
     if (moe_shuffle_plan_arrays_get(NULL, &arrays) != MOE_SHUFFLE_E_INVALID_ARG) return fail("arrays");
     moe_shuffle_plan_destroy(NULL);
+
+    /* the reference copy rejects bad arguments on the host, before any launch */
+    char* const fake = (char*)(uintptr_t)4096; /* never dereferenced */
+    if (moe_shuffle_copy_reference(NULL, fake, 16, NULL) != MOE_SHUFFLE_E_INVALID_ARG) return fail("copy null");
+    if (moe_shuffle_copy_reference(fake, fake + 4096, 24, NULL) != MOE_SHUFFLE_E_ALIGN) return fail("copy size");
+    if (moe_shuffle_copy_reference(fake + 8, fake + 4096, 16, NULL) != MOE_SHUFFLE_E_ALIGN) return fail("copy align");
+    if (moe_shuffle_copy_reference(fake, fake + 16, 64, NULL) != MOE_SHUFFLE_E_INVALID_ARG) return fail("copy overlap");
+    if (moe_shuffle_copy_reference(fake, fake + 16, 0, NULL) != MOE_SHUFFLE_OK) return fail("copy empty");
 
     const int codes[] = {MOE_SHUFFLE_OK, MOE_SHUFFLE_E_INVALID_ARG, MOE_SHUFFLE_E_ALIGN, MOE_SHUFFLE_E_WORKSPACE,
                          MOE_SHUFFLE_E_BAD_INDEX, MOE_SHUFFLE_E_HIP, MOE_SHUFFLE_E_OVERFLOW};

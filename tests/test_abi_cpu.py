@@ -26,7 +26,7 @@ def header_functions():
 def test_every_declared_symbol_is_exported():
     ms, lib = _lib()
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     assert sorted(ms.EXPORTS) == names
     for n in names:
         assert getattr(lib, n) is not None

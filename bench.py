@@ -94,7 +94,7 @@ def copy_bytes_of(T, H, k):
     return min(T * k * H * 2, 2 << 30)
 
 
-def copy_reference(dev, T, H, k):
+def runtime_copy_gbps(dev, T, H, k):
     """The runtime's device-to-device copy of copy_bytes_of(T, H, k) bytes
     (read + write GB/s).  It is also the kernel of known size that scales the
     FETCH_SIZE / WRITE_SIZE counters of a --pmc run."""
@@ -384,7 +384,7 @@ def bench_path(args):
     us = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]) * 1e3)
           for j, n in enumerate(names)}
     B = path_bytes(args.path, T, H, k, N)
-    copy_gbps = copy_reference(dev, T, H, k)
+    copy_gbps = runtime_copy_gbps(dev, T, H, k)
     parity = None
     if not args.no_parity:
         import oracle
@@ -652,7 +652,7 @@ def main():
     B = algorithmic_bytes(T, H, k, N)
     log(f"[bench] {ms_per_step:.3f} ms/step; kernels (us): " + ", ".join(f"{n} {us[n]:.1f}" for n in names))
 
-    copy_gbps = copy_reference(dev, T, H, k)
+    copy_gbps = runtime_copy_gbps(dev, T, H, k)
     ceiling = stream_copy_ceiling(dev)
 
     # The flushed protocol: before each of K reps, an untimed read of 1 GiB

@@ -422,7 +422,7 @@ def bench_path(args):
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(B[dom] / (us[dom] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4), "traffic": None,
                      "alg_bytes_per_launch": B[dom], "avg_launch_us": round(us[dom], 2)},
-        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "runtime_copy_GBps": round(copy_gbps, 1),
         "cpu_baseline": None, "parity": parity, "kernel_src_sha256_16": source_digest(),
     }
     ms.moe_shuffle_plan_destroy(plan)

@@ -20,13 +20,10 @@ namespace ms {
 // One wave per 64-token tile.  hist is column-major [(C+1)][ntiles];
 // column C holds the tile's error flag.
 template <int KMAX>
-__global__ __launch_bounds__(kWave) void plan_count_kernel(const int32_t* __restrict__ idx, int T, int k,
-                                                           int E, FastDiv epr, int C, int ntiles,
-                                                           int32_t* __restrict__ hist)
+__device__ __forceinline__ void count_tile(const int32_t* __restrict__ idx, int T, int k, int E, FastDiv epr, int C,
+                                           int ntiles, int32_t* __restrict__ hist, int tile, int lane,
+                                           unsigned long long* s_mask /* [C], this wave's */)
 {
-    extern __shared__ unsigned long long s_mask[];  // [C]
-    const int lane = threadIdx.x;
-    const int tile = blockIdx.x;
     const int t = tile * kPlanTile + lane;
 
     // The ids first (their load overlaps the clearing of the masks).
@@ -72,6 +69,15 @@ __global__ __launch_bounds__(kWave) void plan_count_kernel(const int32_t* __rest
     const bool any_bad = __ballot(bad) != 0ull;
     const int slots = wave_sum(nslots), placed = wave_sum(ecount);
     if (lane == 0) hist[(int64_t)C * ntiles + tile] = (any_bad || placed != slots) ? 1 : 0;
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(kWave) void plan_count_kernel(const int32_t* __restrict__ idx, int T, int k,
+                                                           int E, FastDiv epr, int C, int ntiles,
+                                                           int32_t* __restrict__ hist)
+{
+    extern __shared__ unsigned long long s_mask[];  // [C]
+    count_tile<KMAX>(idx, T, k, E, epr, C, ntiles, hist, blockIdx.x, threadIdx.x, s_mask);
 }
 
 // ---------------------------------------------------------------- plan_scan
@@ -171,15 +177,10 @@ struct RowWriter {
 };
 
 template <int KMAX>
-__global__ __launch_bounds__(kWave) void plan_place_kernel(PlaceArgs a)
+__device__ __forceinline__ void place_tile(const PlaceArgs& a, int tile, int lane,
+                                           unsigned long long* s_mask /* [C] */, int* s_wbase /* [C] */)
 {
-    extern __shared__ unsigned long long s_dyn[];
     const int C = a.C, E = a.E, R = a.R;
-    unsigned long long* s_mask = s_dyn;     // [C]
-    int* s_wbase = (int*)(s_mask + C);      // [C]
-
-    const int lane = threadIdx.x;
-    const int tile = blockIdx.x;
     const int t = tile * kPlanTile + lane;
     const int k = a.k;
     constexpr int kCols = kMaxCols / kWave;  // histogram columns per lane
@@ -329,11 +330,90 @@ __global__ __launch_bounds__(kWave) void plan_place_kernel(PlaceArgs a)
     rank_rows.finish();
 }
 
+template <int KMAX>
+__global__ __launch_bounds__(kWave) void plan_place_kernel(PlaceArgs a)
+{
+    extern __shared__ unsigned long long s_dyn[];
+    place_tile<KMAX>(a, blockIdx.x, threadIdx.x, s_dyn, (int*)(s_dyn + a.C));
+}
+
+// ---------------------------------------------------------------- small batches
+//
+// Up to kSmallTiles tiles, the three steps run in one block of one wave per
+// tile, separated by block barriers instead of kernel boundaries: one launch
+// instead of three, which is most of the plan's time on a small batch.  The
+// steps are the same functions as above; the scan is one wave per column.
+#ifndef MS_PLAN_SMALL_TILES
+#define MS_PLAN_SMALL_TILES 16
+#endif
+constexpr int kSmallTiles = MS_PLAN_SMALL_TILES;
+static_assert(kSmallTiles <= 16, "the small plan runs one block of at most 16 waves");
+constexpr size_t kSmallLds = 48 * 1024;
+constexpr int kSmallMaxTopK = 16;  // wider rows keep the three launches (registers at 16 waves per block)
+
+template <int KMAX>
+__global__ __launch_bounds__(16 * kWave) void plan_small_kernel(PlaceArgs a, int32_t* __restrict__ hist,
+                                                                         int32_t* __restrict__ tile_base,
+                                                                         int32_t* __restrict__ col_total,
+                                                                         int32_t* __restrict__ status)
+{
+    extern __shared__ unsigned long long s_dyn[];
+    const int C = a.C, ntiles = a.ntiles;
+    const int wave = wave_id(), lane = lane_id();  // one wave per tile: blockDim.x = 64 * ntiles
+    unsigned long long* s_mask = s_dyn + (size_t)wave * C;
+    int* s_wbase = (int*)(s_dyn + (size_t)ntiles * C) + (size_t)wave * C;
+    count_tile<KMAX>(a.idx, a.T, a.k, a.E, a.epr, C, ntiles, hist, wave, lane, s_mask);
+    __syncthreads();  // every tile's histogram is written
+    // Exclusive scan of each column over the tiles (ntiles <= 64: one lane
+    // per tile); column C holds the error flags.
+    for (int c = wave; c <= C; c += ntiles) {
+        const int v = lane < ntiles ? hist[(int64_t)c * ntiles + lane] : 0;
+        if (c == C) {
+            const bool bad = __ballot(v != 0) != 0ull;
+            if (lane == 0) status[0] = bad ? MOE_SHUFFLE_E_BAD_INDEX : MOE_SHUFFLE_OK;
+        } else {
+            const int incl = wave_inclusive_scan(v);
+            if (lane < ntiles) tile_base[(int64_t)c * ntiles + lane] = incl - v;
+            if (lane == kWave - 1) col_total[c] = incl;
+        }
+    }
+    __syncthreads();  // offsets and status are written
+    place_tile<KMAX>(a, wave, lane, s_mask, s_wbase);
+}
+
+static PlaceArgs place_args(const Layout& L, const PlanPtrs& P, FastDiv epr)
+{
+    PlaceArgs a;
+    a.idx = P.idx;
+    a.T = L.T; a.k = L.k; a.E = L.E; a.R = L.R; a.Epr = L.Epr; a.KR = L.KR; a.D = L.D; a.C = L.C;
+    a.ntiles = L.ntiles;
+    a.epr = epr;
+    a.tile_base = P.tile_base; a.col_total = P.col_total; a.status = P.status;
+    a.expert_count = P.expert_count; a.expert_offset = P.expert_offset;
+    a.rank_count = P.rank_count; a.rank_offset = P.rank_offset;
+    a.send_token = P.send_token; a.tok_rank_row = P.tok_rank_row; a.fan_src = P.fan_src;
+    a.fan_dst = P.fan_dst; a.comb_row = P.comb_row;
+    a.rank_segs = P.rank_segs; a.expert_segs = P.expert_segs; a.n_rank_rows = P.n_rank_rows;
+    return a;
+}
+
 hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)
 {
     const int ntiles = L.ntiles;
     const size_t lds_count = sizeof(unsigned long long) * L.C;
     const FastDiv epr = make_fastdiv(L.Epr);
+    const size_t lds_small = (size_t)ntiles * L.C * (sizeof(unsigned long long) + sizeof(int));
+    if (ntiles <= kSmallTiles && lds_small <= kSmallLds && L.k <= kSmallMaxTopK) {
+        const PlaceArgs a = place_args(L, P, epr);
+        const dim3 grid(1), block(ntiles * kWave);
+        if (L.k <= 8)
+            hipLaunchKernelGGL(plan_small_kernel<8>, grid, block, lds_small, s, a, P.tile_hist, P.tile_base,
+                               P.col_total, P.status);
+        else
+            hipLaunchKernelGGL(plan_small_kernel<16>, grid, block, lds_small, s, a, P.tile_hist, P.tile_base,
+                               P.col_total, P.status);
+        return hipGetLastError();
+    }
     if (L.k <= 8)
         hipLaunchKernelGGL(plan_count_kernel<8>, dim3(ntiles), dim3(kWave), lds_count, s, P.idx, L.T, L.k, L.E,
                            epr, L.C, ntiles, P.tile_hist);
@@ -352,17 +432,7 @@ hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)
                        P.tile_base, P.col_total, P.status);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    PlaceArgs a;
-    a.idx = P.idx;
-    a.T = L.T; a.k = L.k; a.E = L.E; a.R = L.R; a.Epr = L.Epr; a.KR = L.KR; a.D = L.D; a.C = L.C;
-    a.ntiles = ntiles;
-    a.epr = epr;
-    a.tile_base = P.tile_base; a.col_total = P.col_total; a.status = P.status;
-    a.expert_count = P.expert_count; a.expert_offset = P.expert_offset;
-    a.rank_count = P.rank_count; a.rank_offset = P.rank_offset;
-    a.send_token = P.send_token; a.tok_rank_row = P.tok_rank_row; a.fan_src = P.fan_src;
-    a.fan_dst = P.fan_dst; a.comb_row = P.comb_row;
-    a.rank_segs = P.rank_segs; a.expert_segs = P.expert_segs; a.n_rank_rows = P.n_rank_rows;
+    const PlaceArgs a = place_args(L, P, epr);
     const size_t lds_place = lds_count + sizeof(int) * L.C;
     if (L.k <= 8)
         hipLaunchKernelGGL(plan_place_kernel<8>, dim3(ntiles), dim3(kWave), lds_place, s, a);

@@ -76,6 +76,28 @@ def test_ragged_and_edge_shapes(T, H, E, k, R):
     harness().check_case(idx, x, w, H, E, R, ye=ye, name=f"ragged-{T}x{H}")
 
 
+# Either side of the limits of the one-launch plan (at most 16 tiles of 64
+# tokens, 48 KiB of masks and bases, top-k <= 16): both plan forms must give
+# the oracle's arrays bit for bit.
+PLAN_FORMS = [
+    # T, H, E, k, R
+    (1024, 64, 32, 8, 8),       # 16 tiles: one launch
+    (1025, 64, 32, 8, 8),       # 17 tiles: three launches
+    (256, 64, 1024 - 64, 8, 64),  # 4 tiles x 1024 columns = 48 KiB: one launch
+    (257, 64, 1024 - 64, 8, 64),  # 5 tiles: three launches
+    (500, 64, 64, 16, 8),       # top-16: one launch
+    (500, 64, 64, 17, 8),       # top-17: three launches
+]
+
+
+@pytest.mark.parametrize("T,H,E,k,R", PLAN_FORMS)
+def test_both_plan_forms(T, H, E, k, R):
+    rng = np.random.default_rng(T * 17 + E + k)
+    idx, w = synth.random_routing(rng, T, E, k, signed_gates=True)
+    x = synth.random_bf16(rng, (T, H))
+    harness().check_case(idx, x, w, H, E, R, name=f"plan-form-{T}-{E}-{k}")
+
+
 def test_all_tokens_one_expert_skew():
     """Every token picks expert 0 first: one segment holds all T rows."""
     rng = np.random.default_rng(5)

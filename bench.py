@@ -691,6 +691,34 @@ def main():
                "tokens_per_s": round(T / (float(np.median(f_dc)) * 1e-6), 1)}
     log(f"[bench] flushed protocol: {flushed}")
 
+    # The same step captured once per rotating batch in a HIP graph and
+    # replayed: one launch call per step instead of four.  Replays run back
+    # to back on the host clock like the timed region above.
+    graphs, gplans = [], []
+    for i in range(nb):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            p = ms.moe_shuffle_plan(dims, idx, ws)
+            ms.moe_shuffle_dispatch_send(p, xs[i], xr)
+            ms.moe_shuffle_dispatch_fanout(p, xr, xe)
+            ms.moe_shuffle_combine(p, xe, w, out)
+        graphs.append(g)
+        gplans.append(p)
+    for i in range(args.warmup):
+        graphs[i % nb].replay()
+    torch.cuda.synchronize()
+    g0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % nb].replay()
+    torch.cuda.synchronize()
+    g_ms = (time.perf_counter() - g0) * 1e3 / args.steps
+    for p in gplans:
+        ms.moe_shuffle_plan_destroy(p)
+    del graphs
+    graph_replay = {"ms_per_step": round(g_ms, 4), "GBps": round(B["total"] / (g_ms * 1e-3) / 1e9, 1),
+                    "tokens_per_s": round(T / (g_ms * 1e-3), 1), "graphs": nb}
+    log(f"[bench] graph replay: {graph_replay}")
+
     parity = None
     if not args.no_parity:
         import oracle
@@ -769,6 +797,7 @@ def main():
         "frac_of_copy_ceiling": round(value / ceiling["GBps"], 4),
         "runtime_copy_GBps": round(copy_gbps, 1),
         "flushed_protocol": flushed,
+        "graph_replay": graph_replay,
         "accumulate": "fp32",
         "roofline": {"kernel": KERNEL_NAMES[dom], "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),

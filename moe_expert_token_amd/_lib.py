@@ -114,8 +114,16 @@ def _ptr(t):
     return t.data_ptr()
 
 
+# The current stream's raw handle without building a torch Stream object
+# (several microseconds per call, which small batches feel).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_cur_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
 def _stream(stream):
     if stream is None:
+        if _raw_stream is not None and _cur_device is not None:
+            return _raw_stream(_cur_device())
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 

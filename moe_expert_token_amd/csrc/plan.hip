@@ -176,9 +176,14 @@ struct RowWriter {
     }
 };
 
+// ct_src[c]: column totals; tb_src[c * tb_stride]: this tile's base in
+// column c; status_src[0]: the plan status (global arrays, or their copies
+// in LDS when the whole plan runs in one block).
 template <int KMAX>
 __device__ __forceinline__ void place_tile(const PlaceArgs& a, int tile, int lane,
-                                           unsigned long long* s_mask /* [C] */, int* s_wbase /* [C] */)
+                                           unsigned long long* s_mask /* [C] */, int* s_wbase /* [C] */,
+                                           const int32_t* ct_src, const int32_t* tb_src, int tb_stride,
+                                           const int32_t* status_src)
 {
     const int C = a.C, E = a.E, R = a.R;
     const int t = tile * kPlanTile + lane;
@@ -188,7 +193,7 @@ __device__ __forceinline__ void place_tile(const PlaceArgs& a, int tile, int lan
     // Every global load first, so their latencies overlap: the status word,
     // this lane's top-k ids, and for each column it owns the column total
     // and this tile's base within the column.
-    const int status = a.status[0];
+    const int status = status_src[0];
     int ev[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) ev[j] = 0x7fffffff;
@@ -202,8 +207,8 @@ __device__ __forceinline__ void place_tile(const PlaceArgs& a, int tile, int lan
 #pragma unroll
     for (int i = 0; i < kCols; ++i) {
         const int c = lane + i * kWave;
-        ct[i] = c < C ? a.col_total[c] : 0;
-        tb[i] = c < C ? a.tile_base[(int64_t)c * a.ntiles + tile] : 0;
+        ct[i] = c < C ? ct_src[c] : 0;
+        tb[i] = c < C ? tb_src[(int64_t)c * tb_stride] : 0;
     }
 
     for (int i = lane; i < C; i += kWave) s_mask[i] = 0ull;
@@ -334,15 +339,19 @@ template <int KMAX>
 __global__ __launch_bounds__(kWave) void plan_place_kernel(PlaceArgs a)
 {
     extern __shared__ unsigned long long s_dyn[];
-    place_tile<KMAX>(a, blockIdx.x, threadIdx.x, s_dyn, (int*)(s_dyn + a.C));
+    place_tile<KMAX>(a, blockIdx.x, threadIdx.x, s_dyn, (int*)(s_dyn + a.C), a.col_total,
+                     a.tile_base + blockIdx.x, a.ntiles, a.status);
 }
 
 // ---------------------------------------------------------------- small batches
 //
 // Up to kSmallTiles tiles, the three steps run in one block of one wave per
-// tile, separated by block barriers instead of kernel boundaries: one launch
-// instead of three, which is most of the plan's time on a small batch.  The
-// steps are the same functions as above; the scan is one wave per column.
+// tile, separated by block barriers instead of kernel boundaries, with the
+// tile histograms, the scanned bases, the column totals and the status in
+// LDS: one launch instead of three and no global round trip between the
+// steps, which is most of the plan's time on a small batch.  The count and
+// place steps are the functions above; the scan is one wave per column.
+// The scan results also go to the workspace for the later kernels.
 #ifndef MS_PLAN_SMALL_TILES
 #define MS_PLAN_SMALL_TILES 16
 #endif
@@ -351,34 +360,56 @@ static_assert(kSmallTiles <= 16, "the small plan runs one block of at most 16 wa
 constexpr size_t kSmallLds = 48 * 1024;
 constexpr int kSmallMaxTopK = 16;  // wider rows keep the three launches (registers at 16 waves per block)
 
+// LDS of the one-block plan: per wave its masks and row bases, then the
+// shared histograms, bases, totals and status.
+static size_t small_plan_lds(int ntiles, int C)
+{
+    return (size_t)ntiles * C * (sizeof(unsigned long long) + sizeof(int)) +
+           sizeof(int) * ((size_t)(C + 1) * ntiles + (size_t)C * ntiles + C + 1);
+}
+
 template <int KMAX>
-__global__ __launch_bounds__(16 * kWave) void plan_small_kernel(PlaceArgs a, int32_t* __restrict__ hist,
-                                                                         int32_t* __restrict__ tile_base,
-                                                                         int32_t* __restrict__ col_total,
-                                                                         int32_t* __restrict__ status)
+__global__ __launch_bounds__(16 * kWave) void plan_small_kernel(PlaceArgs a, int32_t* __restrict__ tile_base,
+                                                                int32_t* __restrict__ col_total,
+                                                                int32_t* __restrict__ status)
 {
     extern __shared__ unsigned long long s_dyn[];
     const int C = a.C, ntiles = a.ntiles;
     const int wave = wave_id(), lane = lane_id();  // one wave per tile: blockDim.x = 64 * ntiles
     unsigned long long* s_mask = s_dyn + (size_t)wave * C;
-    int* s_wbase = (int*)(s_dyn + (size_t)ntiles * C) + (size_t)wave * C;
-    count_tile<KMAX>(a.idx, a.T, a.k, a.E, a.epr, C, ntiles, hist, wave, lane, s_mask);
-    __syncthreads();  // every tile's histogram is written
+    int* s_ints = (int*)(s_dyn + (size_t)ntiles * C);
+    int* s_wbase = s_ints + (size_t)wave * C;
+    int* s_hist = s_ints + (size_t)ntiles * C;      // [(C+1)][ntiles]
+    int* s_tb = s_hist + (size_t)(C + 1) * ntiles;  // [C][ntiles]
+    int* s_ct = s_tb + (size_t)C * ntiles;          // [C]
+    int* s_status = s_ct + C;                       // [1]
+    count_tile<KMAX>(a.idx, a.T, a.k, a.E, a.epr, C, ntiles, s_hist, wave, lane, s_mask);
+    __syncthreads();  // every tile's histogram is in LDS
     // Exclusive scan of each column over the tiles (ntiles <= 64: one lane
     // per tile); column C holds the error flags.
     for (int c = wave; c <= C; c += ntiles) {
-        const int v = lane < ntiles ? hist[(int64_t)c * ntiles + lane] : 0;
+        const int v = lane < ntiles ? s_hist[c * ntiles + lane] : 0;
         if (c == C) {
             const bool bad = __ballot(v != 0) != 0ull;
-            if (lane == 0) status[0] = bad ? MOE_SHUFFLE_E_BAD_INDEX : MOE_SHUFFLE_OK;
+            const int st = bad ? MOE_SHUFFLE_E_BAD_INDEX : MOE_SHUFFLE_OK;
+            if (lane == 0) {
+                s_status[0] = st;
+                status[0] = st;
+            }
         } else {
             const int incl = wave_inclusive_scan(v);
-            if (lane < ntiles) tile_base[(int64_t)c * ntiles + lane] = incl - v;
-            if (lane == kWave - 1) col_total[c] = incl;
+            if (lane < ntiles) {
+                s_tb[c * ntiles + lane] = incl - v;
+                tile_base[(int64_t)c * ntiles + lane] = incl - v;
+            }
+            if (lane == kWave - 1) {
+                s_ct[c] = incl;
+                col_total[c] = incl;
+            }
         }
     }
-    __syncthreads();  // offsets and status are written
-    place_tile<KMAX>(a, wave, lane, s_mask, s_wbase);
+    __syncthreads();  // offsets and status are in LDS
+    place_tile<KMAX>(a, wave, lane, s_mask, s_wbase, s_ct, s_tb + wave, ntiles, s_status);
 }
 
 static PlaceArgs place_args(const Layout& L, const PlanPtrs& P, FastDiv epr)
@@ -402,16 +433,16 @@ hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)
     const int ntiles = L.ntiles;
     const size_t lds_count = sizeof(unsigned long long) * L.C;
     const FastDiv epr = make_fastdiv(L.Epr);
-    const size_t lds_small = (size_t)ntiles * L.C * (sizeof(unsigned long long) + sizeof(int));
+    const size_t lds_small = small_plan_lds(ntiles, L.C);
     if (ntiles <= kSmallTiles && lds_small <= kSmallLds && L.k <= kSmallMaxTopK) {
         const PlaceArgs a = place_args(L, P, epr);
         const dim3 grid(1), block(ntiles * kWave);
         if (L.k <= 8)
-            hipLaunchKernelGGL(plan_small_kernel<8>, grid, block, lds_small, s, a, P.tile_hist, P.tile_base,
-                               P.col_total, P.status);
+            hipLaunchKernelGGL(plan_small_kernel<8>, grid, block, lds_small, s, a, P.tile_base, P.col_total,
+                               P.status);
         else
-            hipLaunchKernelGGL(plan_small_kernel<16>, grid, block, lds_small, s, a, P.tile_hist, P.tile_base,
-                               P.col_total, P.status);
+            hipLaunchKernelGGL(plan_small_kernel<16>, grid, block, lds_small, s, a, P.tile_base, P.col_total,
+                               P.status);
         return hipGetLastError();
     }
     if (L.k <= 8)

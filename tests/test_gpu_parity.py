@@ -77,14 +77,14 @@ def test_ragged_and_edge_shapes(T, H, E, k, R):
 
 
 # Either side of the limits of the one-launch plan (at most 16 tiles of 64
-# tokens, 48 KiB of masks and bases, top-k <= 16): both plan forms must give
-# the oracle's arrays bit for bit.
+# tokens, 48 KiB of LDS, top-k <= 16): both plan forms must give the
+# oracle's arrays bit for bit.
 PLAN_FORMS = [
     # T, H, E, k, R
     (1024, 64, 32, 8, 8),       # 16 tiles: one launch
     (1025, 64, 32, 8, 8),       # 17 tiles: three launches
-    (256, 64, 1024 - 64, 8, 64),  # 4 tiles x 1024 columns = 48 KiB: one launch
-    (257, 64, 1024 - 64, 8, 64),  # 5 tiles: three launches
+    (128, 64, 1024 - 64, 8, 64),  # 2 tiles x 1024 columns, 44 KiB of LDS: one launch
+    (129, 64, 1024 - 64, 8, 64),  # 3 tiles, 64 KiB: three launches
     (500, 64, 64, 16, 8),       # top-16: one launch
     (500, 64, 64, 17, 8),       # top-17: three launches
 ]

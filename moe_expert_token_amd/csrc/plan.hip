@@ -11,6 +11,8 @@
 //               offsets, and gives every (token, rank) and (token, expert)
 //               pair its row: tile base + mbcnt(mask).  Rows come out in
 //               ascending token order inside every segment.
+//   plan_small  the three steps in one block for a batch of at most 16
+//               tiles (one launch instead of three).
 #include "device_common.h"
 
 namespace ms {

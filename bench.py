@@ -12,6 +12,14 @@ Prints one JSON line.  `value` is algorithmic bytes per step / wall time per
 step (GB/s, plan included); algorithmic bytes are what the method must
 move: 2H(T+N) + 2H(N+Tk) + 2H(Tk+T) + 4(N+Tk) + 8Tk, with N the number of
 deduplicated (token, rank) rows.
+
+After the timed region, the same line carries: the per-kernel breakdown
+(HIP events between the calls) and the `roofline` of the fan-out; the
+flushed protocol (memory-side cache evicted before each rep, events around
+plan / dispatch / combine); the measured copy ceiling (the library's
+reference streaming copy of 4 GiB); the step replayed from HIP graphs;
+parity of the last step against the CPU oracle; and the oracle's own
+throughput on the host (`cpu_baseline`).
 """
 
 from __future__ import annotations

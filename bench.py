@@ -97,6 +97,22 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def load_path_traffic(workload: str, path: str, calls):
+    """HBM bytes of the given calls of a --path run (summed), from the
+    committed counter summaries, only while the kernel source matches."""
+    total = 0
+    for call in calls:
+        f = os.path.join(ROOT, "profiles", f"traffic_{path}_{call}_{workload}.json")
+        try:
+            rec = json.load(open(f))
+        except (OSError, ValueError):
+            return None
+        if rec.get("kernel_src_sha256_16") != source_digest():
+            return None
+        total += rec["hbm_bytes_per_call"]
+    return total
+
+
 def copy_bytes_of(T, H, k):
     """Size of the reference copy: a buffer as large as xe, at most 2 GiB."""
     return min(T * k * H * 2, 2 << 30)
@@ -289,6 +305,14 @@ def pmc_path_summary(args, cfg, N, fetch, write, f_factor, w_factor, stats, copy
         us, fb, wb = sum(v[1] for v in mine), sum(v[2] for v in mine), sum(v[3] for v in mine)
         lines.append(f"| {call} | {', '.join(sorted(v[0] for v in mine))} | {us:.1f} | {fb / 1e6:.1f} | "
                      f"{wb / 1e6:.1f} | {B[call] / 1e6:.1f} | {(fb + wb) / B[call]:.3f} |")
+        rec = {"path": args.path, "call": call, "kernels": sorted(v[0] for v in mine), "workload": cfg.name,
+               "kernel_src_sha256_16": digest, "hbm_bytes_per_call": round(fb + wb),
+               "fetch_bytes_per_call": round(fb), "write_bytes_per_call": round(wb),
+               "alg_bytes_per_call": B[call], "traffic_over_alg": round((fb + wb) / B[call], 4),
+               "fetch_scale": round(f_factor, 4), "write_scale": round(w_factor, 4),
+               "copy_kernel_bytes": copy_bytes, "commands": args.commands}
+        with open(os.path.join(args.out_dir, f"traffic_{args.path}_{call}_{cfg.name}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
     lines += ["", "| kernel | avg us (trace) | HBM read MB | HBM write MB |", "|---|---|---|---|"]
     for full, (base, us, fb, wb) in sorted(per.items(), key=lambda kv: -kv[1][1] if kv[1][1] == kv[1][1] else 0):
         lines.append(f"| `{full}` | {us:.1f} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
@@ -417,6 +441,9 @@ def bench_path(args):
     if args.path == "rank-partial-f32":
         B = dict(B, combine_rank_partial_f32=B["total"])
     dom = max(names, key=lambda n: B[n])
+    # the fp32-partial entry point is both calls of its path in one
+    dom_calls = tuple(PATH_KERNELS[args.path]) if dom not in PATH_KERNELS[args.path] else (dom,)
+    traffic = load_path_traffic(cfg.name, args.path, dom_calls)
     value = B["total"] / (ms_per_step * 1e-3) / 1e9
     rec = {
         "metric": f"{args.path} shuffle effective HBM GB/s (fraction of peak), 1 GPU", "value": round(value, 1),
@@ -428,7 +455,7 @@ def bench_path(args):
         "kernel_us": {n: round(us[n], 2) for n in names}, "algorithmic_bytes": B, "accumulate": "fp32",
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(B[dom] / (us[dom] * 1e-6) / 1e9, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(B[dom] / (us[dom] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(B[dom] / (us[dom] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "alg_bytes_per_launch": B[dom], "avg_launch_us": round(us[dom], 2)},
         "runtime_copy_GBps": round(copy_gbps, 1),
         "cpu_baseline": None, "parity": parity, "kernel_src_sha256_16": source_digest(),

@@ -68,7 +68,7 @@ def test_counter_summary_scales_by_the_copy_kernel(tmp_path):
     assert (out / f"kernels_{cfg.name}.md").exists()
 
 
-def test_path_counter_summary_sums_the_kernels_of_each_call(tmp_path):
+def test_path_counter_summary_sums_the_kernels_of_each_call(tmp_path, monkeypatch):
     """--path backward: the three kernels of the combine backward count as
     one call; counters equal to the algorithmic bytes give a ratio of 1."""
     cfg = synth.CONFIGS[0]
@@ -96,10 +96,11 @@ def test_path_counter_summary_sums_the_kernels_of_each_call(tmp_path):
         w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
         for name in parts:
             w.writerow([name + sig, 3, 3000, 1000.0, 20, 900, 1100, 0])
-    out = tmp_path / "out"
+    out = tmp_path / "profiles"
     out.mkdir()
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--pmc-summary", "--path", "backward",
-                        "--config", "0", "--src-sha", "0123456789abcdef", "--fetch-csv", str(tmp_path / "fetch.csv"),
+                        "--config", "0", "--src-sha", bench.source_digest(),
+                        "--fetch-csv", str(tmp_path / "fetch.csv"),
                         "--write-csv", str(tmp_path / "write.csv"), "--trace-stats", str(tmp_path / "stats.csv"),
                         "--out-dir", str(out)], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
@@ -111,6 +112,15 @@ def test_path_counter_summary_sums_the_kernels_of_each_call(tmp_path):
     assert float(calls["combine_bwd"][3]) == pytest.approx(3.0)  # three kernels of 1 us each
     for c in calls.values():
         assert c[7].strip() == "1.000"
+    # one traffic record per call, read back by the bench of that path
+    rec = json.load(open(out / f"traffic_backward_combine_bwd_{cfg.name}.json"))
+    assert rec["hbm_bytes_per_call"] == round(B["combine_bwd"])
+    assert rec["kernels"] == ["combine_bwd_dot_kernel", "combine_bwd_grad_kernel", "gate_grad_kernel"]
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.load_path_traffic(cfg.name, "backward", ("combine_bwd",)) == round(B["combine_bwd"])
+    both = bench.load_path_traffic(cfg.name, "backward", ("sum_expert_rows", "sum_rank_rows"))
+    assert both == round(B["sum_expert_rows"]) + round(B["sum_rank_rows"])
+    assert bench.load_path_traffic(cfg.name, "rank-partial", ("sum_rank_rows",)) is None  # not profiled
 
 
 def test_stored_traffic_is_used_only_for_the_profiled_source(tmp_path, monkeypatch):

@@ -98,6 +98,29 @@ def test_both_plan_forms(T, H, E, k, R):
     harness().check_case(idx, x, w, H, E, R, name=f"plan-form-{T}-{E}-{k}")
 
 
+def _plan_form_shapes(n=40, seed=91):
+    """Seeded shapes around the one-launch plan's limits: up to 18 tiles,
+    top-k up to 20, histograms up to 1024 columns."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < n:
+        R = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+        E = R * int(rng.integers(1, 17))
+        if E + R > 1024:
+            continue
+        k = int(rng.integers(1, min(E, 20) + 1))
+        shapes.append((int(rng.integers(0, 18 * 64 + 1)), 8 * int(rng.integers(1, 40)), E, k, R))
+    return shapes
+
+
+@pytest.mark.parametrize("T,H,E,k,R", _plan_form_shapes())
+def test_random_shapes_around_plan_forms(T, H, E, k, R):
+    rng = np.random.default_rng(T * 13 + H * 5 + E * 3 + k + R)
+    idx, w = synth.random_routing(rng, T, E, k, signed_gates=True)
+    x = synth.random_bf16(rng, (T, H))
+    harness().check_case(idx, x, w, H, E, R, name=f"plan-rand-{T}-{E}-{k}", query_first=bool(T % 2))
+
+
 def test_all_tokens_one_expert_skew():
     """Every token picks expert 0 first: one segment holds all T rows."""
     rng = np.random.default_rng(5)

@@ -187,6 +187,10 @@ __global__ __launch_bounds__(kBlock) void gate_grad_kernel(const float* __restri
 #ifndef MS_CBWD_DOT_UNIT
 #define MS_CBWD_DOT_UNIT 2
 #endif
+// The gate gradient's summation order (8U products per lane, the lane tree,
+// then the 512U-element chunks) is part of the stated arithmetic, and the
+// tolerance it is tested against assumes U = 1 or 2.
+static_assert(MS_CBWD_DOT_UNIT == 1 || MS_CBWD_DOT_UNIT == 2, "the gate-gradient pass sums at U = 1 or 2");
 // Pass order: grad_ye first.  With plain loads the partials first measured
 // 0.900 against 0.878 ms per backward step (DeepSeek-V3-like); with
 // non-temporal loads the order makes no difference (0.833 against 0.831).

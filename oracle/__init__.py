@@ -61,6 +61,8 @@ class Oracle:
         self.lib.oracle_combine_rank_partial.argtypes = [ctypes.POINTER(_Dims), vp, vp, vp, ctypes.c_int32, vp, vp,
                                                          vp, vp]
         self.lib.oracle_combine_rank_partial_f32.argtypes = self.lib.oracle_combine_rank_partial.argtypes
+        self.lib.oracle_round_bf16.argtypes = [vp, vp, ctypes.c_int64]
+        self.lib.oracle_round_bf16.restype = None
         for f in (self.lib.oracle_check_dims, self.lib.oracle_plan, self.lib.oracle_dispatch,
                   self.lib.oracle_combine, self.lib.oracle_dispatch_backward, self.lib.oracle_combine_backward,
                   self.lib.oracle_combine_rank_partial, self.lib.oracle_combine_rank_partial_f32):
@@ -105,6 +107,13 @@ class Oracle:
         a["fan_src"] = a["fan_src"][:T * k]
         a["fan_dst"] = a["fan_dst"][:N]
         return rc, a
+
+    def round_bf16(self, bits: np.ndarray) -> np.ndarray:
+        """The fp32 -> bf16 rounding step alone, on fp32 bit patterns (uint32)."""
+        bits = np.ascontiguousarray(bits, dtype=np.uint32)
+        out = np.zeros(bits.shape, np.uint16)
+        self.lib.oracle_round_bf16(bits.ctypes.data, out.ctypes.data, bits.size)
+        return out
 
     def dispatch(self, plan: dict, x: np.ndarray, E: int, k: int, R: int):
         x = np.ascontiguousarray(x, dtype=np.uint16)

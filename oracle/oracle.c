@@ -242,6 +242,20 @@ static uint16_t f32_to_bf16_rne(float f)
     return (uint16_t)keep;
 }
 
+/* The rounding that ends every stored bf16 row, on its own, so that tests
+ * can pin it on inputs no sum produces (signalling NaNs, values next to the
+ * overflow threshold): out[i] = f32_to_bf16_rne(the fp32 value with bits
+ * in[i]).  The bits are taken as integers so that nothing on the way changes
+ * a NaN. */
+void oracle_round_bf16(const uint32_t* in, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float f;
+        memcpy(&f, &in[i], sizeof f);
+        out[i] = f32_to_bf16_rne(f);
+    }
+}
+
 /*
  * Combine: out[t][h] = bf16( sum over j = 0..k-1 of w[t][j] * ye[comb_row[t][j]][h] ),
  * summed in fp32 from +0 in ascending j with one fused multiply-add per term.

@@ -198,6 +198,83 @@ def combine_exact(comb_row: np.ndarray, ye_bits: np.ndarray, w: np.ndarray) -> n
     return out
 
 
+# --------------------------------------------------------------------------
+# the fp32 -> bf16 rounding step on its own
+# --------------------------------------------------------------------------
+
+def bf16_is_nan(b: np.ndarray) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint16)
+    return ((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0)
+
+
+def bf16_nearest_even(bits: np.ndarray) -> np.ndarray:
+    """bf16 of finite or infinite fp32 values (uint32 bit patterns), decided
+    by value: the two bf16 neighbours of |v| (the truncation, and the next
+    value away from zero one bf16 ulp further, 2^128 past the largest finite
+    one) are compared by their float64 distance to |v|; a tie goes to the
+    neighbour with an even last significand bit; 2^128 is infinity.  Every
+    quantity is exact in float64.  NaN inputs are not handled here."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint32)
+    assert not np.any(((bits & 0x7F800000) == 0x7F800000) & ((bits & 0x007FFFFF) != 0))
+    sign = (bits >> 16) & 0x8000
+    mag = bits & np.uint32(0x7FFFFFFF)
+    v = mag.view(np.float32).astype(np.float64)
+    lo_bits = mag & np.uint32(0xFFFF0000)
+    lo = lo_bits.view(np.float32).astype(np.float64)
+    expo = (lo_bits >> 23).astype(np.int64)
+    ulp = np.ldexp(1.0, np.maximum(expo, 1) - 127 - 7)        # bf16 spacing at lo (subnormals: 2^-133)
+    inf = np.isinf(v)
+    v = np.where(inf, 0.0, v)                                  # decided below; keeps the distances finite
+    lo = np.where(inf, 0.0, lo)
+    d_lo, d_hi = v - lo, (lo + ulp) - v
+    lo16 = (lo_bits >> 16).astype(np.uint32)
+    up = (d_hi < d_lo) | ((d_hi == d_lo) & ((lo16 & 1) == 1))
+    res = np.where(inf, 0x7F80, np.where(up, lo16 + 1, lo16))   # lo16 + 1 past 0x7F7F is 0x7F80: infinity
+    return (res | sign).astype(np.uint16)
+
+
+# (fp32 bits, bf16 bits) fixed by the IEEE 754 rules for a narrowing
+# conversion: nearest, ties to even, overflow to infinity with the sign,
+# a NaN stays a NaN (made quiet) with its sign.
+ROUND_TABLE = [
+    (0x00000000, 0x0000), (0x80000000, 0x8000),          # zeros keep their sign
+    (0x3F808000, 0x3F80), (0x3F818000, 0x3F82),          # ties: even stays, odd goes up
+    (0x3F808001, 0x3F81), (0xBF808001, 0xBF81),          # just above a tie
+    (0x00008000, 0x0000), (0x00018000, 0x0002),          # ties among fp32 subnormals
+    (0x00017FFF, 0x0001), (0x80008001, 0x8001),
+    (0x007FFFFF, 0x0080),                                 # largest fp32 subnormal rounds up to 2^-126
+    (0x7F7F7FFF, 0x7F7F),                                 # below the half-way point: the largest bf16
+    (0x7F7F8000, 0x7F80), (0xFF7F8000, 0xFF80),          # half-way, odd: to infinity
+    (0x7F7FFFFF, 0x7F80), (0xFF7FFFFF, 0xFF80),          # the largest fp32 overflows bf16
+    (0x7F800000, 0x7F80), (0xFF800000, 0xFF80),          # infinities
+]
+# fp32 NaN bits -> (sign of the bf16 NaN): every one must stay a quiet NaN
+NAN_TABLE = [(0x7F800001, 0), (0xFF800001, 1), (0x7FC00000, 0), (0xFFC00000, 1), (0x7F80FFFF, 0),
+             (0x7FBFFFFF, 0), (0xFFFFFFFF, 1), (0x7F810000, 0)]
+
+
+def check_round_bf16(orc) -> None:
+    """The oracle's rounding step against the IEEE table above and against
+    bf16_nearest_even on 2^18 random finite fp32 patterns (every binade, both
+    signs, subnormals, and patterns next to each tie)."""
+    src = np.array([a for a, _ in ROUND_TABLE], np.uint32)
+    np.testing.assert_array_equal(orc.round_bf16(src), np.array([b for _, b in ROUND_TABLE], np.uint16))
+    np.testing.assert_array_equal(bf16_nearest_even(src), np.array([b for _, b in ROUND_TABLE], np.uint16))
+    nan = np.array([a for a, _ in NAN_TABLE], np.uint32)
+    got = orc.round_bf16(nan)
+    assert np.all(bf16_is_nan(got)), [hex(v) for v in got]
+    assert np.all((got & 0x0040) != 0), "NaN not made quiet"
+    np.testing.assert_array_equal(got >> 15, np.array([s for _, s in NAN_TABLE], np.uint16))
+    rng = np.random.default_rng(4242)
+    r = rng.integers(0, 1 << 32, size=1 << 18, dtype=np.uint64).astype(np.uint32)
+    r = r[((r & 0x7F800000) != 0x7F800000)]                    # finite only
+    near = (r & np.uint32(0xFFFF0000)) | np.uint32(0x8000)     # exact ties and their neighbours
+    near = np.concatenate([near, near + 1, near - 1])
+    near = near[((near & 0x7F800000) != 0x7F800000)]
+    r = np.concatenate([r, near])
+    np.testing.assert_array_equal(orc.round_bf16(r), bf16_nearest_even(r))
+
+
 def bf16_ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     """|ord(a) - ord(b)| on bf16 bit patterns; +0 and -0 are equal."""
     def ordkey(u):
@@ -239,6 +316,7 @@ def run_battery(orc) -> None:
     import os
     import synth
     here = os.path.dirname(os.path.abspath(__file__))
+    check_round_bf16(orc)
     g = json.load(open(os.path.join(here, "golden", "fig3_two_tokens.json")))
     d, ex = g["dims"], g["expected"]
     idx = np.array(g["topk_idx"], np.int32)

@@ -26,23 +26,59 @@ def _setup(idx, H=64, E=8, R=4):
     return ms, h, torch, dims, ws, plan
 
 
+# Bad rows for both forms of the plan: the one-launch form (at most 16
+# tiles of 64 tokens, top-k <= 16) and the three-launch form (count, scan,
+# place), whose status travels from the count kernel's error column through
+# the scan to the place kernel's early exit.
+BAD_CASES = [
+    # name, T, E, k, R, rows made bad
+    ("one-launch", 300, 8, 2, 4, (137,)),
+    ("three-launch-tiles", 1100, 8, 2, 4, (1050,)),          # 18 tiles, the bad row in tile 16
+    ("three-launch-topk-first", 500, 32, 17, 4, (3,)),       # top-17, the bad row in tile 0
+    ("three-launch-topk-last", 500, 32, 17, 4, (499,)),      # ... and in the last, ragged tile
+]
+
+WS_FILL = 0x5A  # workspace bytes before the plan: index arrays must keep them
+
+
+@pytest.mark.parametrize("form,T,E,k,R,rows", BAD_CASES)
 @pytest.mark.parametrize("bad", ["out_of_range", "negative", "duplicate"])
-def test_bad_index_sets_status_and_blocks_writes(bad):
-    rng = np.random.default_rng(1)
-    idx, w = synth.random_routing(rng, 300, 8, 2)
-    idx[137] = {"out_of_range": [1, 8], "negative": [-1, 3], "duplicate": [5, 5]}[bad]
-    ms, h, torch, dims, ws, plan = _setup(idx)
+def test_bad_index_sets_status_and_blocks_writes(form, T, E, k, R, rows, bad):
+    import torch
+    import moe_expert_token_amd as ms
+    import gpu_harness as h
+    rng = np.random.default_rng(T + k)
+    H = 64
+    idx, w = synth.random_routing(rng, T, E, k)
+    for r in rows:
+        if bad == "out_of_range":
+            idx[r, k - 1] = E
+        elif bad == "negative":
+            idx[r, 0] = -1
+        else:
+            idx[r, k - 1] = idx[r, 0]
+    h.say(f"[errors] bad ids ({bad}) in rows {rows}, {form}: T={T} E={E} k={k} R={R}")
+    dims = ms.dims_of(T, H, E, k, R)
+    ws = torch.full((ms.moe_shuffle_workspace_size(dims),), WS_FILL, dtype=torch.uint8, device="cuda")
+    plan = ms.moe_shuffle_plan(dims, torch.from_numpy(idx).cuda(), ws)
     info = ms.moe_shuffle_plan_query(plan)
     assert info["status"] == ms.E_BAD_INDEX
-    xr = torch.full((300 * 2, 64), h.SENTINEL, dtype=torch.int16, device="cuda")
-    xe = torch.full((300 * 2, 64), h.SENTINEL, dtype=torch.int16, device="cuda")
-    out = torch.full((300, 64), h.SENTINEL, dtype=torch.int16, device="cuda")
-    x = h.to_dev16(synth.random_bf16(rng, (300, 64)))
+    KR = min(k, R)
+    xr = torch.full((T * KR, H), h.SENTINEL, dtype=torch.int16, device="cuda")
+    xe = torch.full((T * k, H), h.SENTINEL, dtype=torch.int16, device="cuda")
+    out = torch.full((T, H), h.SENTINEL, dtype=torch.int16, device="cuda")
+    x = h.to_dev16(synth.random_bf16(rng, (T, H)))
     ms.moe_shuffle_dispatch(plan, x, xr, xe)
     ms.moe_shuffle_combine(plan, xe, torch.from_numpy(w).cuda(), out)
     torch.cuda.synchronize()
     for t in (xr, xe, out):
         assert bool((t == h.SENTINEL).all())
+    # the place step wrote no row index either
+    fill = int(np.array([WS_FILL] * 4, np.uint8).view(np.int32)[0])
+    v = ms.plan_array_views(plan, T * KR)
+    for key in ("comb_row", "fan_dst", "fan_src", "send_token", "tok_rank_row", "expert_offset", "rank_offset"):
+        assert bool((v[key] == fill).all()), f"{key} was written"
+    ms.moe_shuffle_plan_destroy(plan)
 
 
 def test_host_side_argument_errors():

@@ -58,6 +58,15 @@ MUTANTS = {
                             "sum = sum + g[q] * bf16_to_f32(ye[q * H + h]);"),
     "partial_f32_ranks_descending": ("for (int r = 0; r < KR; ++r) {\n                const int64_t p = tok_rank_row[t * KR + r];\n                if (p < 0) break;",
                                      "for (int r = KR - 1; r >= 0; --r) {\n                const int64_t p = tok_rank_row[t * KR + r];\n                if (p < 0) continue;"),
+    "round_nan_to_inf": ("if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);", ""),
+    "round_nan_drops_sign": ("if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);",
+                             "if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)(((u >> 16) & 0x7fffu) | 0x0040u);"),
+    "round_nan_not_quieted": ("if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);",
+                              "if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)(u >> 16);"),
+    "round_saturates": ("    if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;\n    return (uint16_t)keep;",
+                        "    if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;\n"
+                        "    if ((keep & 0x7fffu) == 0x7f80u && (u & 0x7fffffffu) < 0x7f800000u) keep -= 1u;\n"
+                        "    return (uint16_t)keep;"),
     "flush_subnormals": ("uint32_t u = (uint32_t)b << 16;\n    float f;",
                          "uint32_t u = (uint32_t)b << 16;\n    if ((u & 0x7f800000u) == 0) u &= 0x80000000u;\n    float f;"),
 }

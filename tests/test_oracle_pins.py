@@ -265,3 +265,20 @@ def test_error_codes(orc):
     assert orc.plan(bad, 8, 8, 4)[0] == oracle.E_BAD_INDEX
     assert orc.plan(np.array([[3, 3]], np.int32), 8, 8, 4)[0] == oracle.E_BAD_INDEX
     assert orc.plan(np.array([[-1, 2]], np.int32), 8, 8, 4)[0] == oracle.E_BAD_INDEX
+
+
+# ---------------------------------------------------------------- the rounding step
+
+def test_round_bf16_ieee_table_and_definition(orc):
+    """fp32 -> bf16 on its own: an IEEE table (ties to even, overflow to
+    infinity with the sign, a NaN whose payload sits only in the low half
+    stays a NaN, NaNs keep their sign and come out quiet) and the
+    nearest-even rule decided by float64 distances on 2^18 random patterns."""
+    pins.check_round_bf16(orc)
+
+
+def test_round_bf16_low_payload_nan_is_not_infinity(orc):
+    """The classic slip of adding the rounding bias to a NaN: 0x7f800001 has
+    its payload in the dropped half and would carry into infinity."""
+    got = orc.round_bf16(np.array([0x7F800001, 0xFF800001, 0x7F80FFFF], np.uint32))
+    assert np.all(pins.bf16_is_nan(got)) and list(got >> 15) == [0, 1, 0]

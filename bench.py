@@ -553,62 +553,19 @@ def bench_pipelined(args):
     print(json.dumps(rec), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, help="workload id (0..4); default: DeepSeek-V3-like")
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-budget-s", type=float, default=12.0, help="CPU-oracle timing budget")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-parity", action="store_true")
-    ap.add_argument("--chunks", type=int, default=4, help="token chunks for --path pipelined")
-    ap.add_argument("--path", default="forward",
-                    choices=("forward", "backward", "rank-partial", "rank-partial-f32", "pipelined"),
-                    help="forward (default): plan + dispatch + combine; backward: combine and dispatch backward; "
-                         "rank-partial: combine through one row per (token, rank); rank-partial-f32: the same "
-                         "with fp32 partial rows")
-    ap.add_argument("--pmc-summary", action="store_true", help="summarise rocprofv3 CSVs into profiles/ (no GPU)")
-    ap.add_argument("--fetch-csv")
-    ap.add_argument("--write-csv")
-    ap.add_argument("--trace-stats")
-    ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
-    ap.add_argument("--commands", nargs="*", default=[])
-    ap.add_argument("--src-sha", default=None, help="kernel source hash of the profiled run (default: current)")
-    args = ap.parse_args()
-    if args.pmc_summary:
-        pmc_summary(args)
-        return
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: the shuffle runs its expert-parallel ranks as logical "
-              f"partitions of one GPU's HBM (asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
-              file=sys.stderr)
-        sys.exit(2)
-
+def forward_run(args, cfg_id, dev, full=True, ceiling=None):
+    """The forward step (plan + send + fan-out + combine) on workload cfg_id:
+    the timed region, the per-kernel event breakdown, the flushed protocol,
+    the graph replay and the parity of the last step against the oracle.
+    With full, also the runtime copy and (unless given) the measured copy
+    ceiling, and the CPU baseline.  Returns the record of the JSON line."""
     import numpy as np
     import torch
 
     import moe_expert_token_amd as ms
     import synth
 
-    if not os.path.exists(ms.LIB_PATH):
-        from moe_expert_token_amd import build as hip_build
-        hip_build.build()
-    ms.load()
-    if not torch.cuda.is_available():
-        raise SystemExit("bench.py needs a GPU")
-    dev = torch.device("cuda:0")
-    if args.path == "pipelined":
-        bench_pipelined(args)
-        return
-    if args.path != "forward":
-        bench_path(args)
-        return
-
-    cfg = synth.CONFIGS[args.config]
+    cfg = synth.CONFIGS[cfg_id]
     T, H, E, k, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.R
     KR = min(k, R)
     log(f"[bench] workload {cfg.name}: generating inputs")
@@ -687,8 +644,9 @@ def main():
     B = algorithmic_bytes(T, H, k, N)
     log(f"[bench] {ms_per_step:.3f} ms/step; kernels (us): " + ", ".join(f"{n} {us[n]:.1f}" for n in names))
 
-    copy_gbps = runtime_copy_gbps(dev, T, H, k)
-    ceiling = stream_copy_ceiling(dev)
+    copy_gbps = runtime_copy_gbps(dev, T, H, k) if full else None
+    if ceiling is None:
+        ceiling = stream_copy_ceiling(dev)
 
     # The flushed protocol: before each of K reps, an untimed read of 1 GiB
     # evicts the 256 MB memory-side cache (a read leaves no dirty lines to be
@@ -778,7 +736,7 @@ def main():
         log(f"[bench] parity vs oracle: {parity}")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if full and not args.no_cpu_baseline:
         import oracle
         orc = oracle.get()
         allowed = sorted(os.sched_getaffinity(0))
@@ -830,7 +788,7 @@ def main():
         "algorithmic_bytes": B,
         "copy_ceiling": ceiling,
         "frac_of_copy_ceiling": round(value / ceiling["GBps"], 4),
-        "runtime_copy_GBps": round(copy_gbps, 1),
+        "runtime_copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
         "flushed_protocol": flushed,
         "graph_replay": graph_replay,
         "accumulate": "fp32",
@@ -842,7 +800,103 @@ def main():
         "kernel_src_sha256_16": source_digest(),
     }
     ms.moe_shuffle_plan_destroy(last_plan)
-    print(json.dumps(rec), flush=True)
+    del xs, x0, idx, w, ws, xr, xe, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+
+
+def config_summary(rec):
+    """The per-workload figures of a forward record, for the per_config object."""
+    f, g, c = rec["flushed_protocol"], rec["graph_replay"], rec["config"]
+    return {
+        "workload": c["workload"], "T": c["T"], "H": c["H"], "E": c["E"], "k": c["k"], "R": c["R"], "N": c["N"],
+        "algorithmic_bytes": rec["algorithmic_bytes"]["total"],
+        "ms_per_step": rec["ms_per_step"], "GBps": rec["value"], "frac_of_peak": rec["frac_of_peak"],
+        "tokens_per_s": rec["tokens_per_s"],
+        "kernel_us": rec["kernel_us"],
+        "dispatch_combine_GBps": rec["dispatch_combine_GBps"],
+        "dispatch_combine_frac_of_peak": rec["dispatch_combine_frac_of_peak"],
+        "flushed": {"t_plan_us": f["t_plan_us"], "t_dispatch_us": f["t_dispatch_us"],
+                    "t_combine_us": f["t_combine_us"], "dc_us_p10_p50_p90": f["dc_us_p10_p50_p90"],
+                    "dispatch_combine_GBps": f["dispatch_combine_GBps"], "frac_of_peak": f["frac_of_peak"],
+                    "frac_of_copy_ceiling": f["frac_of_copy_ceiling"], "tokens_per_s": f["tokens_per_s"]},
+        "graph_replay": {"ms_per_step": g["ms_per_step"], "GBps": g["GBps"], "tokens_per_s": g["tokens_per_s"]},
+        "roofline_frac": rec["roofline"]["frac"],
+        "parity": rec["parity"],
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload id (0..4); default: DeepSeek-V3-like")
+    ap.add_argument("--per-config", default="0,1,2,3,4",
+                    help="workloads whose figures go into the per_config object of the forward line "
+                         "(comma-separated ids, or none)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0, help="CPU-oracle timing budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--chunks", type=int, default=4, help="token chunks for --path pipelined")
+    ap.add_argument("--path", default="forward",
+                    choices=("forward", "backward", "rank-partial", "rank-partial-f32", "pipelined"),
+                    help="forward (default): plan + dispatch + combine; backward: combine and dispatch backward; "
+                         "rank-partial: combine through one row per (token, rank); rank-partial-f32: the same "
+                         "with fp32 partial rows")
+    ap.add_argument("--pmc-summary", action="store_true", help="summarise rocprofv3 CSVs into profiles/ (no GPU)")
+    ap.add_argument("--fetch-csv")
+    ap.add_argument("--write-csv")
+    ap.add_argument("--trace-stats")
+    ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--commands", nargs="*", default=[])
+    ap.add_argument("--src-sha", default=None, help="kernel source hash of the profiled run (default: current)")
+    args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the shuffle runs its expert-parallel ranks as logical "
+              f"partitions of one GPU's HBM (asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import moe_expert_token_amd as ms
+
+    if not os.path.exists(ms.LIB_PATH):
+        from moe_expert_token_amd import build as hip_build
+        hip_build.build()
+    ms.load()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    if args.path == "pipelined":
+        bench_pipelined(args)
+        return
+    if args.path != "forward":
+        bench_path(args)
+        return
+
+    head = forward_run(args, args.config, dev, full=True)
+    ids = [int(c) for c in args.per_config.split(",") if c.strip()] if args.per_config != "none" else []
+    if ids:
+        per = {}
+        for cid in ids:
+            if cid == args.config:
+                per[str(cid)] = config_summary(head)
+            else:
+                per[str(cid)] = config_summary(forward_run(args, cid, dev, full=False,
+                                                           ceiling=head["copy_ceiling"]))
+        head["per_config"] = per
+    print(json.dumps(head), flush=True)
 
 
 if __name__ == "__main__":

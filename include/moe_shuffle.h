@@ -257,6 +257,45 @@ int moe_shuffle_combine_rank_partial_f32(moe_shuffle_plan_t plan, const void* ye
 int moe_shuffle_combine_backward(moe_shuffle_plan_t plan, const void* grad_out, const void* ye, const float* topk_w,
                                  void* grad_ye, float* grad_w, void* stream);
 
+/* ---- allocation-free planning ----
+ * For callers that cannot allocate memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The same plan as
+ * moe_shuffle_plan, with two differences:
+ *  - the workspace is a static device buffer of
+ *    MOE_SHUFFLE_STATIC_WORKSPACE_BYTES that the library holds on every GPU
+ *    it runs on, until the process ends;
+ *  - the host handle is built in the caller's `storage`.
+ * The call allocates nothing: no hipMalloc or hipFree, no host heap, no
+ * library routine that allocates.  Its first call on a device looks up the
+ * buffer's address on that device, once.
+ *   dims, topk_idx  as for moe_shuffle_plan.
+ *   stream  a stream of the current device (NULL: its null stream).
+ *   storage caller-owned host memory for the handle; it must outlive every
+ *           use of the plan.
+ *   plan    out: the handle, which points into storage.  Every other call
+ *           takes it like any plan.  moe_shuffle_plan_destroy on it frees
+ *           nothing.
+ * There is one buffer per GPU, shared by every call:
+ *  - each moe_shuffle_plan_static on a GPU overwrites it, so an earlier
+ *    static plan on that GPU is invalid from then on;
+ *  - calls on one GPU that overlap in time (other streams, other threads)
+ *    race on it.
+ * Nothing in it needs clearing between calls: every word a call reads was
+ * written earlier by its plan or by the call itself.
+ * Errors: as for moe_shuffle_plan, plus:
+ *  - MOE_SHUFFLE_E_WORKSPACE when these dims need more than
+ *    MOE_SHUFFLE_STATIC_WORKSPACE_BYTES (moe_shuffle_workspace_size tells);
+ *    nothing is launched and the buffer keeps its contents;
+ *  - MOE_SHUFFLE_E_INVALID_ARG for a stream of another device. */
+#define MOE_SHUFFLE_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+typedef struct {
+    uint64_t opaque[64];
+} moe_shuffle_plan_storage;
+
+int moe_shuffle_plan_static(const moe_shuffle_dims* dims, const int32_t* topk_idx, void* stream,
+                            moe_shuffle_plan_storage* storage, moe_shuffle_plan_t* plan);
+
 /* Synchronises `stream`, reads N and the status word back to the host.
  * Returns the plan's status (MOE_SHUFFLE_OK or MOE_SHUFFLE_E_BAD_INDEX). */
 int moe_shuffle_plan_query(moe_shuffle_plan_t plan, void* stream, moe_shuffle_plan_info* info);

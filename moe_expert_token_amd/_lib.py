@@ -26,8 +26,10 @@ EXPORTS = (
     "moe_shuffle_last_hip_error", "moe_shuffle_sum_expert_rows", "moe_shuffle_sum_rank_rows",
     "moe_shuffle_dispatch_backward", "moe_shuffle_combine_rank_partial", "moe_shuffle_combine_backward",
     "moe_shuffle_dispatch_range", "moe_shuffle_combine_range", "moe_shuffle_combine_rank_partial_f32",
-    "moe_shuffle_copy_reference",
+    "moe_shuffle_copy_reference", "moe_shuffle_plan_static",
 )
+
+STATIC_WORKSPACE_BYTES = 64 << 20  # MOE_SHUFFLE_STATIC_WORKSPACE_BYTES
 
 
 class MoeShuffleError(RuntimeError):
@@ -50,6 +52,11 @@ class PlanInfo(ctypes.Structure):
 
 
 _vp = ctypes.c_void_p
+
+
+class PlanStorage(ctypes.Structure):
+    """Host storage for the handle of moe_shuffle_plan_static."""
+    _fields_ = [("opaque", ctypes.c_uint64 * 64)]
 
 
 class PlanArrays(ctypes.Structure):
@@ -92,6 +99,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_shuffle_dispatch_range": (ctypes.c_int, [_vp, _vp, _vp, i64, _vp, ctypes.c_int32, ctypes.c_int32, _vp]),
         "moe_shuffle_combine_range": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp]),
         "moe_shuffle_copy_reference": (ctypes.c_int, [_vp, _vp, ctypes.c_size_t, _vp]),
+        "moe_shuffle_plan_static": (ctypes.c_int, [ctypes.POINTER(Dims), _vp, _vp, ctypes.POINTER(PlanStorage),
+                                                   ctypes.POINTER(_vp)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -176,6 +185,20 @@ def moe_shuffle_plan(dims: Dims, topk_idx, workspace, stream=None) -> Plan:
                                  ctypes.byref(h))
     _check("moe_shuffle_plan", rc)
     return Plan(h.value, dims, workspace, topk_idx)
+
+
+def moe_shuffle_plan_static(dims: Dims, topk_idx, stream=None) -> Plan:
+    """The plan in the library's static workspace (no device allocation); the
+    returned Plan holds the handle's storage.  A later static plan on the same
+    GPU invalidates this one."""
+    h = _vp(0)
+    storage = PlanStorage()
+    rc = load().moe_shuffle_plan_static(ctypes.byref(dims), _ptr(topk_idx), _stream(stream), ctypes.byref(storage),
+                                        ctypes.byref(h))
+    _check("moe_shuffle_plan_static", rc)
+    plan = Plan(h.value, dims, None, topk_idx)
+    plan.storage = storage
+    return plan
 
 
 def moe_shuffle_dispatch(plan: Plan, x, xr, xe, stream=None):

@@ -7,6 +7,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "internal.h"
 #include "moe_shuffle.h"
 
@@ -15,7 +17,19 @@ struct moe_shuffle_plan_s {
     ms::Layout L;
     char* ws;
     int64_t n_known;  // N after moe_shuffle_plan_query, else -1
+    int owned;        // 1: allocated by moe_shuffle_plan (destroy frees it); 0: in caller storage
 };
+
+static_assert(sizeof(moe_shuffle_plan_s) <= sizeof(moe_shuffle_plan_storage),
+              "the plan handle must fit the caller's storage");
+static_assert(alignof(moe_shuffle_plan_s) <= alignof(moe_shuffle_plan_storage),
+              "the caller's storage must be aligned for the plan handle");
+
+// The workspace of moe_shuffle_plan_static: one per GPU, held until the
+// process ends.  In host code this name is only a stand-in, not a device
+// address: host code never passes it to a kernel or a copy; it uses the
+// address that hipGetSymbolAddress gives on each device (static_scratch).
+static __device__ __align__(256) unsigned char scratch[MOE_SHUFFLE_STATIC_WORKSPACE_BYTES];
 
 namespace {
 
@@ -118,24 +132,18 @@ int moe_shuffle_workspace_size(const moe_shuffle_dims* dims, size_t* bytes)
     return MOE_SHUFFLE_OK;
 }
 
-int moe_shuffle_plan(const moe_shuffle_dims* dims, const int32_t* topk_idx, void* workspace, size_t workspace_bytes,
-                     void* stream, moe_shuffle_plan_t* plan)
-{
-    int rc = check_dims(dims);
-    if (rc) return rc;
-    if (!plan || !workspace || (dims->num_tokens > 0 && !topk_idx)) return MOE_SHUFFLE_E_INVALID_ARG;
-    if (misaligned(workspace, 256) || misaligned(topk_idx, 4)) return MOE_SHUFFLE_E_ALIGN;
-    ms::Layout L;
-    ms::make_layout(*dims, L);
-    if (workspace_bytes < L.total) return MOE_SHUFFLE_E_WORKSPACE;
+}  // extern "C"
 
-    moe_shuffle_plan_s* p = (moe_shuffle_plan_s*)calloc(1, sizeof(moe_shuffle_plan_s));
-    if (!p) return MOE_SHUFFLE_E_INVALID_ARG;
+namespace {
+
+// Fills the handle and launches the plan's kernels into its workspace.
+hipError_t launch_plan_into(moe_shuffle_plan_s* p, const moe_shuffle_dims* dims, const ms::Layout& L,
+                            const int32_t* topk_idx, char* workspace, void* stream)
+{
     p->dims = *dims;
     p->L = L;
-    p->ws = (char*)workspace;
+    p->ws = workspace;
     p->n_known = -1;
-
     ms::PlanPtrs P;
     P.idx = topk_idx;
     P.status = at<int32_t>(p, L.status);
@@ -154,11 +162,95 @@ int moe_shuffle_plan(const moe_shuffle_dims* dims, const int32_t* topk_idx, void
     P.tile_hist = at<int32_t>(p, L.tile_hist);
     P.tile_base = at<int32_t>(p, L.tile_base);
     P.col_total = at<int32_t>(p, L.col_total);
-    const hipError_t e = ms::launch_plan(L, P, (hipStream_t)stream);
+    return ms::launch_plan(L, P, (hipStream_t)stream);
+}
+
+// Checks shared by both plan entry points; fills L.
+int check_plan_args(const moe_shuffle_dims* dims, const int32_t* topk_idx, const moe_shuffle_plan_t* plan,
+                    ms::Layout* L)
+{
+    const int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!plan || (dims->num_tokens > 0 && !topk_idx)) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (misaligned(topk_idx, 4)) return MOE_SHUFFLE_E_ALIGN;
+    ms::make_layout(*dims, *L);
+    return MOE_SHUFFLE_OK;
+}
+
+// The address of `scratch` on each device, looked up once per device (with
+// that device current) by static_scratch.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// The static workspace on the device of `stream` (which must be the current
+// device).
+int static_scratch(void* stream, char** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+        if (e != hipSuccess) return hip_fail(e);
+        if (sdev != dev) return MOE_SHUFFLE_E_INVALID_ARG;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        if (!ptr || misaligned(ptr, 256)) return MOE_SHUFFLE_E_ALIGN;
+        g_scratch[dev] = ptr;
+    }
+    *out = (char*)g_scratch[dev];
+    return MOE_SHUFFLE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_shuffle_plan(const moe_shuffle_dims* dims, const int32_t* topk_idx, void* workspace, size_t workspace_bytes,
+                     void* stream, moe_shuffle_plan_t* plan)
+{
+    ms::Layout L;
+    int rc = check_plan_args(dims, topk_idx, plan, &L);
+    if (rc) return rc;
+    if (!workspace) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (misaligned(workspace, 256)) return MOE_SHUFFLE_E_ALIGN;
+    if (workspace_bytes < L.total) return MOE_SHUFFLE_E_WORKSPACE;
+
+    moe_shuffle_plan_s* p = (moe_shuffle_plan_s*)calloc(1, sizeof(moe_shuffle_plan_s));
+    if (!p) return MOE_SHUFFLE_E_INVALID_ARG;
+    p->owned = 1;
+    const hipError_t e = launch_plan_into(p, dims, L, topk_idx, (char*)workspace, stream);
     if (e != hipSuccess) {
         free(p);
         return hip_fail(e);
     }
+    *plan = p;
+    return MOE_SHUFFLE_OK;
+}
+
+int moe_shuffle_plan_static(const moe_shuffle_dims* dims, const int32_t* topk_idx, void* stream,
+                            moe_shuffle_plan_storage* storage, moe_shuffle_plan_t* plan)
+{
+    ms::Layout L;
+    int rc = check_plan_args(dims, topk_idx, plan, &L);
+    if (rc) return rc;
+    if (!storage) return MOE_SHUFFLE_E_INVALID_ARG;
+    if (L.total > MOE_SHUFFLE_STATIC_WORKSPACE_BYTES) return MOE_SHUFFLE_E_WORKSPACE;
+    char* ws = nullptr;
+    rc = static_scratch(stream, &ws);
+    if (rc) return rc;
+    memset(storage, 0, sizeof *storage);
+    moe_shuffle_plan_s* p = (moe_shuffle_plan_s*)(void*)storage;
+    p->owned = 0;
+    const hipError_t e = launch_plan_into(p, dims, L, topk_idx, ws, stream);
+    if (e != hipSuccess) return hip_fail(e);
     *plan = p;
     return MOE_SHUFFLE_OK;
 }
@@ -492,7 +584,10 @@ int moe_shuffle_copy_reference(const void* src, void* dst, size_t bytes, void* s
     return e == hipSuccess ? MOE_SHUFFLE_OK : hip_fail(e);
 }
 
-void moe_shuffle_plan_destroy(moe_shuffle_plan_t plan) { free(plan); }
+void moe_shuffle_plan_destroy(moe_shuffle_plan_t plan)
+{
+    if (plan && plan->owned) free(plan);
+}
 
 const char* moe_shuffle_strerror(int code)
 {

@@ -26,7 +26,7 @@ def header_functions():
 def test_every_declared_symbol_is_exported():
     ms, lib = _lib()
     names = header_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     assert sorted(ms.EXPORTS) == names
     for n in names:
         assert getattr(lib, n) is not None
@@ -109,3 +109,29 @@ def test_header_is_c_and_host_entry_points_link_from_c(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.strip().splitlines()[-1] == "ok"
+
+
+def test_static_plan_argument_errors_on_the_host():
+    """The allocation-free plan rejects bad arguments and oversize dims
+    before any device work (so these run without a GPU)."""
+    import ctypes as C
+    ms, lib = _lib()
+    st = ms.PlanStorage()
+    h = C.c_void_p(0)
+    ok = ms.dims_of(4, 8, 8, 2, 4)
+    idx = (C.c_int32 * 8)()
+    assert lib.moe_shuffle_plan_static(C.byref(ok), idx, None, None, C.byref(h)) == ms.E_INVALID_ARG
+    assert lib.moe_shuffle_plan_static(C.byref(ok), idx, None, C.byref(st), None) == ms.E_INVALID_ARG
+    assert lib.moe_shuffle_plan_static(C.byref(ok), None, None, C.byref(st), C.byref(h)) == ms.E_INVALID_ARG
+    assert lib.moe_shuffle_plan_static(C.byref(ms.dims_of(4, 12, 8, 2, 4)), idx, None, C.byref(st),
+                                       C.byref(h)) == ms.E_ALIGN
+    # the largest batch of the tests needs more than the static workspace holds
+    big = ms.dims_of(262144, 7168, 256, 8, 32)
+    assert ms.moe_shuffle_workspace_size(big) > ms.STATIC_WORKSPACE_BYTES
+    assert lib.moe_shuffle_plan_static(C.byref(big), idx, None, C.byref(st), C.byref(h)) == ms.E_WORKSPACE
+    assert h.value is None
+    # every one of the five workloads fits
+    import synth
+    for cfg in synth.CONFIGS.values():
+        assert ms.moe_shuffle_workspace_size(ms.dims_of(cfg.T, cfg.H, cfg.E, cfg.k, cfg.R)) <= \
+            ms.STATIC_WORKSPACE_BYTES, cfg.name

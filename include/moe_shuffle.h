@@ -113,8 +113,11 @@ typedef struct {
     int32_t fan_dst_width;  /* D */
 } moe_shuffle_plan_arrays;
 
-/* Bytes of device workspace a plan with these dims needs (host only, no
- * device work).  Errors: INVALID_ARG, ALIGN, OVERFLOW for bad dims. */
+/* Boundary helper, not a step of the method: the bytes of caller-owned
+ * device workspace a plan with these dims needs.  The workspace holds the
+ * plan's logical segments and row maps (FUSCO press summary, Group 3) and
+ * the scratch of the later calls.  Host only, no device work.  Errors:
+ * INVALID_ARG, ALIGN, OVERFLOW for bad dims. */
 int moe_shuffle_workspace_size(const moe_shuffle_dims* dims, size_t* bytes);
 
 /*
@@ -296,11 +299,16 @@ typedef struct {
 int moe_shuffle_plan_static(const moe_shuffle_dims* dims, const int32_t* topk_idx, void* stream,
                             moe_shuffle_plan_storage* storage, moe_shuffle_plan_t* plan);
 
-/* Synchronises `stream`, reads N and the status word back to the host.
- * Returns the plan's status (MOE_SHUFFLE_OK or MOE_SHUFFLE_E_BAD_INDEX). */
+/* Boundary helper, not a step of the method.  Synchronises `stream` and
+ * reads back N, the size of the rank-major (device-major) buffer of the
+ * exchange (FUSCO abstract), and the status word.  Returns the plan's
+ * status (MOE_SHUFFLE_OK or MOE_SHUFFLE_E_BAD_INDEX); after it, xr may be
+ * sized at exactly N rows. */
 int moe_shuffle_plan_query(moe_shuffle_plan_t plan, void* stream, moe_shuffle_plan_info* info);
 
-/* Device pointers of the plan arrays (no device work, no sync). */
+/* Boundary helper, not a step of the method: the device pointers of the
+ * plan arrays, i.e. the logical segment descriptors (FUSCO press summary,
+ * Group 3) and the row maps.  No device work, no sync. */
 int moe_shuffle_plan_arrays_get(moe_shuffle_plan_t plan, moe_shuffle_plan_arrays* arrays);
 
 /* ---- measurement helper (not a step of the shuffle) ----
@@ -316,13 +324,17 @@ int moe_shuffle_plan_arrays_get(moe_shuffle_plan_t plan, moe_shuffle_plan_arrays
  * `stream`. */
 int moe_shuffle_copy_reference(const void* src, void* dst, size_t bytes, void* stream);
 
-/* Frees the host handle (not the workspace).  NULL is ignored. */
+/* Boundary helper, not a step of the method: frees the host handle of
+ * moe_shuffle_plan (not the workspace).  NULL and handles of
+ * moe_shuffle_plan_static are ignored. */
 void moe_shuffle_plan_destroy(moe_shuffle_plan_t plan);
 
-/* Static text for a status code. */
+/* Boundary helper, not a step of the method: static text for a status
+ * code. */
 const char* moe_shuffle_strerror(int code);
 
-/* The hipError_t of the calling thread's last MOE_SHUFFLE_E_HIP. */
+/* Boundary helper, not a step of the method: the hipError_t of the
+ * calling thread's last MOE_SHUFFLE_E_HIP. */
 int moe_shuffle_last_hip_error(void);
 
 #ifdef __cplusplus

@@ -266,6 +266,78 @@ def pmc_summary(args):
     print("\n".join(lines))
 
 
+def counter_summary(args):
+    """Turns rocprofv3 --pmc passes of one command (any counters among
+    GRBM_GUI_ACTIVE, SQ_WAVES, SQ_WAVE_CYCLES, SQ_BUSY_CYCLES,
+    SQ_WAIT_INST_ANY, TCC_EA0_RDREQ(_LEVEL), TCC_EA0_WRREQ(_LEVEL),
+    TCP_TCC_READ_REQ(_LATENCY), TCP_PENDING_STALL_CYCLES, TA_TA_BUSY, ...)
+    into a markdown table per kernel under profiles/: the raw per-dispatch
+    means and the derived occupancy, stall and latency figures.  The
+    GRBM_GUI_ACTIVE value of a dispatch is the sum over the XCDs, so one
+    XCD's busy cycles are that divided by their count (from the agent info)."""
+    import csv
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(list)
+    agent = {}
+    for path in args.counter_csv:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            if args.kernel_filter and not any(f in name for f in args.kernel_filter):
+                continue
+            counter = r["Counter_Name"][:-4] if r["Counter_Name"].endswith("_sum") else r["Counter_Name"]
+            vals[name][counter].append(float(r["Counter_Value"]))
+            dur[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        info = os.path.join(os.path.dirname(path), "pmc_agent_info.csv")
+        if os.path.exists(info):
+            for row in csv.DictReader(open(info)):
+                if row.get("Name", "").startswith("gfx"):
+                    agent = row
+    xcc, cus, wpc = int(agent.get("Num_Xcc", 8)), int(agent.get("Cu_Count", 256)), int(agent.get("Max_Waves_Per_Cu", 32))
+    lines = [f"# Counters — {args.title}", "", "Commands (run from the repository root on one MI355X):", ""]
+    lines += [f"    {c}" for c in args.commands] + [""]
+    lines += [f"Device: {agent.get('Name', '?')}, {cus} CUs in {xcc} XCDs, at most {wpc} waves per CU.  "
+              "Each figure is the mean over the kernel's dispatches in these runs.", "",
+              "Derived figures (cycles of one XCD: G = GRBM_GUI_ACTIVE / XCDs):",
+              "- occupancy = 4 * SQ_WAVE_CYCLES / (G * CUs * waves per CU) (SQ_WAVE_CYCLES counts 4-cycle units);",
+              "- issue wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES;",
+              "- L1 -> L2 read latency = TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ (cycles), and reads in flight "
+              "per CU = TCP_TCC_READ_REQ_LATENCY / (G * CUs);",
+              "- TCP pending stall = TCP_PENDING_STALL_CYCLES / (G * CUs); TA busy = TA_TA_BUSY / (G * CUs);",
+              "- L2 -> memory read latency = TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ (cycles), and reads in flight in "
+              "the whole device = TCC_EA0_RDREQ_LEVEL / G (writes alike).", ""]
+    hdr = ("| kernel | dispatches | mean us | occupancy | issue wait | L1->L2 read latency | reads in flight / CU | "
+           "TCP pending stall | TA busy | L2->mem read latency | mem reads in flight | mem writes in flight |")
+    lines += [hdr, "|" + "---|" * (hdr.count("|") - 1)]
+    raw = ["", "Raw counters (means per dispatch):", ""]
+
+    def fmt(x, f="{:.2f}"):
+        return "-" if x is None else f.format(x)
+    for name in sorted(vals, key=lambda n: -sum(dur[n]) / len(dur[n])):
+        v = {c: sum(x) / len(x) for c, x in vals[name].items()}
+        g = v.get("GRBM_GUI_ACTIVE")
+        G = g / xcc if g else None
+
+        def q(num, den):
+            return v[num] / den if num in v and den else None
+        occ = q("SQ_WAVE_CYCLES", G * cus * wpc / 4) if G else None
+        wait = q("SQ_WAIT_INST_ANY", v.get("SQ_WAVE_CYCLES"))
+        lat = q("TCP_TCC_READ_REQ_LATENCY", v.get("TCP_TCC_READ_REQ"))
+        infl = q("TCP_TCC_READ_REQ_LATENCY", G * cus) if G else None
+        pend = q("TCP_PENDING_STALL_CYCLES", G * cus) if G else None
+        ta = q("TA_TA_BUSY", G * cus) if G else None
+        elat = q("TCC_EA0_RDREQ_LEVEL", v.get("TCC_EA0_RDREQ"))
+        erd = q("TCC_EA0_RDREQ_LEVEL", G) if G else None
+        ewr = q("TCC_EA0_WRREQ_LEVEL", G) if G else None
+        lines.append(f"| `{name}` | {len(dur[name])} | {sum(dur[name]) / len(dur[name]):.1f} | {fmt(occ)} | "
+                     f"{fmt(wait)} | {fmt(lat, '{:.0f}')} | {fmt(infl, '{:.1f}')} | {fmt(pend)} | {fmt(ta)} | "
+                     f"{fmt(elat, '{:.0f}')} | {fmt(erd, '{:.0f}')} | {fmt(ewr, '{:.0f}')} |")
+        raw.append(f"- `{name}`: " + ", ".join(f"{c} {x:.4g}" for c, x in sorted(v.items())))
+    with open(os.path.join(args.out_dir, args.out_name), "w") as f:
+        f.write("\n".join(lines + raw) + "\n")
+    print("\n".join(lines + raw))
+
+
 # The kernels that make up each call of the other paths (by kernel name).
 PATH_KERNELS = {
     "backward": {"combine_bwd": ("combine_bwd_grad_kernel", "combine_bwd_dot_kernel", "gate_grad_kernel"),
@@ -855,9 +927,18 @@ def main():
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--commands", nargs="*", default=[])
     ap.add_argument("--src-sha", default=None, help="kernel source hash of the profiled run (default: current)")
+    ap.add_argument("--counter-summary", action="store_true",
+                    help="summarise rocprofv3 --pmc CSVs of any counters into profiles/ (no GPU)")
+    ap.add_argument("--counter-csv", nargs="*", default=[])
+    ap.add_argument("--kernel-filter", nargs="*", default=[])
+    ap.add_argument("--out-name", default="counters.md")
+    ap.add_argument("--title", default="")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args)
+        return
+    if args.counter_summary:
+        counter_summary(args)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -270,7 +270,8 @@ int moe_shuffle_combine_backward(moe_shuffle_plan_t plan, const void* grad_out, 
  *  - the host handle is built in the caller's `storage`.
  * The call allocates nothing: no hipMalloc or hipFree, no host heap, no
  * library routine that allocates.  Its first call on a device looks up the
- * buffer's address on that device, once.
+ * buffer's address on that device, once: make that call before capturing
+ * later ones into a HIP graph.
  *   dims, topk_idx  as for moe_shuffle_plan.
  *   stream  a stream of the current device (NULL: its null stream).
  *   storage caller-owned host memory for the handle; it must outlive every

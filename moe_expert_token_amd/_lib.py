@@ -303,6 +303,9 @@ def moe_shuffle_last_hip_error() -> int:
 
 def plan_array_views(plan: Plan, N: int | None = None) -> dict:
     """int32 views of the plan arrays inside the workspace tensor (no copy)."""
+    if plan.workspace is None:
+        raise ValueError("a plan of moe_shuffle_plan_static lives in the library's static buffer, not in a "
+                         "workspace tensor; read its arrays through moe_shuffle_plan_arrays_get")
     a = moe_shuffle_plan_arrays_get(plan)
     ws = plan.workspace
     base = ws.data_ptr()

@@ -35,6 +35,7 @@ BAD_CASES = [
     ("one-launch", 300, 8, 2, 4, (137,)),
     ("one-launch-last-tile", 1024, 8, 2, 4, (1023,)),       # 16 tiles, the bad row in the last
     ("three-launch-tiles", 1100, 8, 2, 4, (1050,)),          # 18 tiles, the bad row in tile 16
+    ("three-launch-last-tile", 4096, 8, 2, 4, (4095,)),      # 64 tiles, the bad row in the last
     ("three-launch-mid-size", 4200, 8, 2, 4, (4150,)),       # 66 tiles, the bad row in tile 64
     ("three-launch-topk-first", 500, 32, 17, 4, (3,)),       # top-17, the bad row in tile 0
     ("three-launch-topk-last", 500, 32, 17, 4, (499,)),      # ... and in the last, ragged tile

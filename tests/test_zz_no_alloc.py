@@ -134,3 +134,59 @@ def test_static_plan_matches_workspace_plan_twice_then_refuses_oversize():
     assert arrays["rank_offset"][-1] == got2["N"]
     info = ms.moe_shuffle_plan_query(plan2)
     assert info["status"] == 0 and info["N"] == got2["N"]
+
+
+def test_static_plan_replays_in_a_graph():
+    """The allocation-free plan under HIP graph capture, its purpose: plan,
+    dispatch and combine captured once (the device's first static plan made
+    before the capture) and replayed with new routing and activations in the
+    captured buffers; every replay must give the bits of the same step run
+    eagerly with a workspace plan."""
+    import gpu_harness as h
+    import torch
+
+    import moe_expert_token_amd as ms
+    T, H, E, k, R = 1000, 1032, 32, 4, 8
+    rng = np.random.default_rng(31)
+    dims = ms.dims_of(T, H, E, k, R)
+    idx_d = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w_d = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    x_d = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    bufs = [torch.zeros(shape, dtype=torch.int16, device="cuda") for shape in ((T * min(k, R), H), (T * k, H), (T, H))]
+    ref = [torch.zeros_like(b) for b in bufs]
+    ws = torch.empty(ms.moe_shuffle_workspace_size(dims), dtype=torch.uint8, device="cuda")
+
+    def load_inputs():
+        idx, w = synth.random_routing(rng, T, E, k, signed_gates=True)
+        idx_d.copy_(torch.from_numpy(idx))
+        w_d.copy_(torch.from_numpy(w))
+        x_d.copy_(h.to_dev16(synth.random_bf16(rng, (T, H))))
+
+    def step(plan, out_bufs):
+        xr, xe, out = out_bufs
+        ms.moe_shuffle_dispatch(plan, x_d, xr, xe)
+        ms.moe_shuffle_combine(plan, xe, w_d, out)
+        return plan
+
+    load_inputs()
+    step(ms.moe_shuffle_plan_static(dims, idx_d), bufs)   # the first call on the device, outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = step(ms.moe_shuffle_plan_static(dims, idx_d), bufs)
+    torch.cuda.synchronize()
+    for replay in range(4):
+        load_inputs()
+        eager = step(ms.moe_shuffle_plan(dims, idx_d, ws), ref)
+        N = ms.moe_shuffle_plan_query(eager)["N"]
+        for b in bufs:
+            b.fill_(0x3F80)                   # eager work between the replays, and stale contents
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert ms.moe_shuffle_plan_query(captured)["N"] == N
+        for name, got, want in zip(("xr", "xe", "out"), bufs, ref):
+            n = N if name == "xr" else got.shape[0]
+            assert torch.equal(got[:n], want[:n]), f"replay {replay}: {name}"
+        h.say(f"[no-alloc] graph replay {replay} N={N} matches the eager step")
+        ms.moe_shuffle_plan_destroy(eager)

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <new>
 
 #include "internal.h"
 #include "moe_shuffle.h"
@@ -246,8 +247,8 @@ int moe_shuffle_plan_static(const moe_shuffle_dims* dims, const int32_t* topk_id
     char* ws = nullptr;
     rc = static_scratch(stream, &ws);
     if (rc) return rc;
-    memset(storage, 0, sizeof *storage);
-    moe_shuffle_plan_s* p = (moe_shuffle_plan_s*)(void*)storage;
+    // the handle lives in the caller's storage (placement new: no allocation)
+    moe_shuffle_plan_s* p = new (static_cast<void*>(storage)) moe_shuffle_plan_s{};
     p->owned = 0;
     const hipError_t e = launch_plan_into(p, dims, L, topk_idx, ws, stream);
     if (e != hipSuccess) return hip_fail(e);

@@ -258,8 +258,15 @@ MS_REDUCE_KERNEL(sum_rank_rows_kernel, MS_SUMR_NT_LOAD, MS_SUMR_NT_STORE)
 #ifndef MS_SUMX_UNIT
 #define MS_SUMX_UNIT 2  // measured: 279 us against 338 us at U = 1 (DeepSeek-V3-like)
 #endif
+// The sender's sum gathers a token's rank rows at 2 KiB units.  At 1 KiB it
+// is faster only while the memory system still holds the state its own
+// previous call left (155 against 162 us, DeepSeek-V3-like): after the
+// combine backward, or a 1 GiB copy, in between, 1 KiB units take 187 and
+// 168 us, while 2 KiB units take 162-164 us whatever ran before.  In the
+// training direction the combine backward (and, in a model, the expert
+// GEMMs) runs before it, so the 2 KiB unit is the faster one there too.
 #ifndef MS_SUMR_UNIT
-#define MS_SUMR_UNIT 1
+#define MS_SUMR_UNIT 2
 #endif
 
 // The receiver's sum keeps 2 KiB units over large sources too: 1306 us

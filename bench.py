@@ -277,8 +277,12 @@ def counter_summary(args):
     XCD's busy cycles are that divided by their count (from the agent info)."""
     import csv
     import collections
+    if not args.title or not args.commands:
+        raise SystemExit("--counter-summary needs --title and --commands (the rocprofv3 lines that wrote the CSVs)")
+    digest = args.src_sha or source_digest()
     vals = collections.defaultdict(lambda: collections.defaultdict(list))
     dur = collections.defaultdict(list)
+    seen = collections.defaultdict(set)
     agent = {}
     for path in args.counter_csv:
         for r in csv.DictReader(open(path)):
@@ -287,14 +291,17 @@ def counter_summary(args):
                 continue
             counter = r["Counter_Name"][:-4] if r["Counter_Name"].endswith("_sum") else r["Counter_Name"]
             vals[name][counter].append(float(r["Counter_Value"]))
-            dur[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            if (path, r["Dispatch_Id"]) not in seen[name]:  # one row per counter of a dispatch
+                seen[name].add((path, r["Dispatch_Id"]))
+                dur[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         info = os.path.join(os.path.dirname(path), "pmc_agent_info.csv")
         if os.path.exists(info):
             for row in csv.DictReader(open(info)):
                 if row.get("Name", "").startswith("gfx"):
                     agent = row
     xcc, cus, wpc = int(agent.get("Num_Xcc", 8)), int(agent.get("Cu_Count", 256)), int(agent.get("Max_Waves_Per_Cu", 32))
-    lines = [f"# Counters — {args.title}", "", "Commands (run from the repository root on one MI355X):", ""]
+    lines = [f"# Counters — {args.title} (kernel source sha256[:16] {digest})", "",
+             "Commands (run from the repository root on one MI355X):", ""]
     lines += [f"    {c}" for c in args.commands] + [""]
     lines += [f"Device: {agent.get('Name', '?')}, {cus} CUs in {xcc} XCDs, at most {wpc} waves per CU.  "
               "Each figure is the mean over the kernel's dispatches in these runs.", "",

@@ -142,3 +142,56 @@ def test_algorithmic_bytes_count_each_step_once():
     assert b["fanout"] == row * (2 + 2) + 4 * 2         # read 2 rank rows, write 2 expert rows
     assert b["combine"] == row * (2 + 1) + 8 * 2        # read 2 expert rows, write 1, rows + gates
     assert b["total"] == b["send"] + b["fanout"] + b["combine"]
+
+
+def test_occupancy_and_latency_summary_derives_each_figure(tmp_path):
+    """--counter-summary: each derived column follows its stated formula
+    from the per-dispatch means (G = GRBM_GUI_ACTIVE / XCDs), a dispatch
+    counts once however many counter rows it has, the "_sum" suffix of a
+    counter name is dropped, and the title carries the kernel source hash."""
+    G, cus, wpc, xcc = 1000.0, 256, 32, 8
+    counters = {
+        "GRBM_GUI_ACTIVE": G * xcc,
+        "SQ_WAVE_CYCLES": 0.5 * G * cus * wpc / 4,      # occupancy 0.50
+        "SQ_WAIT_INST_ANY": 0.25 * 0.5 * G * cus * wpc / 4,  # issue wait 0.25
+        "TCP_TCC_READ_REQ_sum": 1000.0,
+        "TCP_TCC_READ_REQ_LATENCY_sum": 1000.0 * 1500,  # 1500 cycles; 5.9 reads in flight per CU
+        "TCP_PENDING_STALL_CYCLES_sum": 0.75 * G * cus,  # 0.75
+        "TA_TA_BUSY_sum": 0.5 * G * cus,                 # 0.50
+        "TCC_EA0_RDREQ_sum": 2000.0,
+        "TCC_EA0_RDREQ_LEVEL_sum": 2000.0 * 2000,        # 2000 cycles; 4000 reads in flight
+        "TCC_EA0_WRREQ_LEVEL_sum": 3000.0 * G,           # 3000 writes in flight
+    }
+    name = "void ms::combine_rows_kernel<1, true, 1, 4, 8, 1, 0>(unsigned int __vector(4) const*)"
+    d = tmp_path / "pass"
+    d.mkdir()
+    with open(d / "pmc_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"])
+        for i, (c, v) in enumerate(counters.items()):  # two dispatches, one row per counter each
+            w.writerow([1, name, c, v, 1000, 1000 + 183000])
+            w.writerow([2, name, c, v, 1000, 1000 + 185000])
+        w.writerow([3, "void ms::plan_count_kernel<8>(int const*)", "GRBM_GUI_ACTIVE", 1.0, 0, 1000])
+    with open(d / "pmc_agent_info.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Node_Id", "Name", "Num_Xcc", "Cu_Count", "Max_Waves_Per_Cu"])
+        w.writerow([0, "AMD EPYC", 0, 0, 0])
+        w.writerow([1, "gfx950", xcc, cus, wpc])
+    out = tmp_path / "out"
+    out.mkdir()
+    base = [sys.executable, os.path.join(ROOT, "bench.py"), "--counter-summary", "--counter-csv",
+            str(d / "pmc_counter_collection.csv"), "--kernel-filter", "combine_rows", "--out-dir", str(out),
+            "--out-name", "c.md", "--src-sha", "0123456789abcdef"]
+    r = subprocess.run(base, capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "--commands" in r.stderr, "a summary without its commands is refused"
+    r = subprocess.run(base + ["--title", "combine", "--commands", "rocprofv3 --pmc ..."], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    text = (out / "c.md").read_text()
+    assert text.splitlines()[0] == "# Counters — combine (kernel source sha256[:16] 0123456789abcdef)"
+    assert "    rocprofv3 --pmc ..." in text
+    rows = [ln for ln in text.splitlines() if ln.startswith("| `")]
+    assert len(rows) == 1 and "plan_count" not in text  # the filter keeps the combine only
+    cells = [c.strip() for c in rows[0].strip("|").split("|")]
+    assert cells[0] == "`ms::combine_rows_kernel<1, true, 1, 4, 8, 1, 0>`"
+    assert cells[1:] == ["2", "184.0", "0.50", "0.25", "1500", "5.9", "0.75", "0.50", "2000", "4000", "3000"]

@@ -791,20 +791,26 @@ def forward_run(args, cfg_id, dev, full=True, ceiling=None):
                     "tokens_per_s": round(T / (g_ms * 1e-3), 1), "graphs": nb}
     log(f"[bench] graph replay: {graph_replay}")
 
-    parity = None
+    parity, oracle_s = None, None
     if not args.no_parity:
         import oracle
         orc = oracle.get()
+        o0 = time.perf_counter()
         rc, o = orc.plan(inp["topk_idx"], H, E, R)
+        o1 = time.perf_counter()
         v = ms.plan_array_views(last_plan, N)
         plan_ok = rc == 0 and o["N"] == N and all(
             np.array_equal(v[key].cpu().numpy(), o[key])
             for key in ("send_token", "tok_rank_row", "fan_src", "fan_dst", "comb_row", "expert_offset",
                         "rank_offset", "rank_segs", "expert_segs"))
+        o2 = time.perf_counter()
         oxr, oxe = orc.dispatch(o, inp["x"], E, k, R)
+        o3 = time.perf_counter()
         xr_ok = np.array_equal(xr[:N].cpu().numpy().view(np.uint16), oxr)
         xe_ok = np.array_equal(xe.cpu().numpy().view(np.uint16), oxe)
+        o4 = time.perf_counter()
         oout = orc.combine(o["comb_row"], oxe, inp["topk_w"], E, R)
+        o5 = time.perf_counter()
         got = out.cpu().numpy().view(np.uint16)
         # the identity expert (ye = xe) with gates summing to 1 returns x, -0 as +0
         x_rt = np.where(inp["x"] == 0x8000, 0, inp["x"]).astype(np.uint16)
@@ -812,7 +818,10 @@ def forward_run(args, cfg_id, dev, full=True, ceiling=None):
                   "out_max_ulp": int(np.abs(bf16_order(got) - bf16_order(oout)).max()),
                   "out_ndiff": int((got != oout).sum()), "out_bitexact": bool(np.array_equal(got, oout)),
                   "roundtrip_bitexact": bool(np.array_equal(got, x_rt))}
-        log(f"[bench] parity vs oracle: {parity}")
+        # the oracle calls of this check, timed once (single-threaded C, not pinned)
+        oracle_s = {"plan": round(o1 - o0, 4), "dispatch": round(o3 - o2, 4), "combine": round(o5 - o4, 4),
+                    "cores": 1, "host_cpus": os.cpu_count()}
+        log(f"[bench] parity vs oracle: {parity}; oracle seconds {oracle_s}")
 
     cpu = None
     if full and not args.no_cpu_baseline:
@@ -876,6 +885,7 @@ def forward_run(args, cfg_id, dev, full=True, ceiling=None):
                      "traffic": traffic, "alg_bytes_per_launch": B[dom], "avg_launch_us": round(us[dom], 2)},
         "cpu_baseline": cpu,
         "parity": parity,
+        "oracle_s": oracle_s,
         "kernel_src_sha256_16": source_digest(),
     }
     ms.moe_shuffle_plan_destroy(last_plan)
@@ -905,6 +915,7 @@ def config_summary(rec):
         "graph_replay": {"ms_per_step": g["ms_per_step"], "GBps": g["GBps"], "tokens_per_s": g["tokens_per_s"]},
         "roofline_frac": rec["roofline"]["frac"],
         "parity": rec["parity"],
+        "oracle_s": rec["oracle_s"],
     }
 
 

@@ -25,6 +25,7 @@ throughput on the host (`cpu_baseline`).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -572,6 +573,33 @@ def bench_pipelined(args):
     bounds = [0] + [b for b in bounds if b > 0]
     a = torch.cuda.current_stream()
     bstream = torch.cuda.Stream()
+    cu_split, masked = None, []
+    if args.cu_split > 0:
+        # The dispatch stream on the first CUs of the mask, the combine stream
+        # on the rest (HIP's CU-masked streams; each takes a hardware queue of
+        # its own, so the run needs GPU_MAX_HW_QUEUES above the default 4).
+        props = torch.cuda.get_device_properties(dev)
+        ncu = props.multi_processor_count
+        nd = max(1, min(ncu - 1, int(round(args.cu_split * ncu))))
+        words = (ncu + 31) // 32
+
+        def mask_of(lo, hi):
+            m = [0] * words
+            for c in range(lo, hi):
+                m[c // 32] |= 1 << (c % 32)
+            return (ctypes.c_uint32 * words)(*m)
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                     ctypes.POINTER(ctypes.c_uint32)]
+        for lo, hi in ((0, nd), (nd, ncu)):
+            h = ctypes.c_void_p()
+            rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), words, mask_of(lo, hi))
+            if rc != 0:
+                raise SystemExit(f"hipExtStreamCreateWithCUMask failed with HIP error {rc}")
+            masked.append(h)
+        a = torch.cuda.ExternalStream(masked[0].value, device=dev)
+        bstream = torch.cuda.ExternalStream(masked[1].value, device=dev)
+        cu_split = {"dispatch_cus": nd, "combine_cus": ncu - nd}
 
     def step_seq(i):
         p = ms.moe_shuffle_plan(dims, idx, ws)
@@ -580,7 +608,9 @@ def bench_pipelined(args):
         return p
 
     def step_pipe(i):
-        p = ms.moe_shuffle_plan(dims, idx, ws)
+        if masked:  # the plan, too, on the dispatch stream, after the previous step's combine
+            a.wait_stream(torch.cuda.current_stream())
+        p = ms.moe_shuffle_plan(dims, idx, ws, stream=a)
         x = xs[i % nb]
         for t0, t1 in zip(bounds[:-1], bounds[1:]):
             ms.moe_shuffle_dispatch_range(p, x, xr, xe, t0, t1, stream=a)
@@ -589,6 +619,8 @@ def bench_pipelined(args):
             bstream.wait_event(ev)
             ms.moe_shuffle_combine_range(p, xe, w, out, t0, t1, stream=bstream)
         a.wait_stream(bstream)
+        if masked:
+            torch.cuda.current_stream().wait_stream(a)
         return p
 
     def timed(fn):
@@ -619,13 +651,18 @@ def bench_pipelined(args):
                   "xe_bitexact": bool(np.array_equal(xe.cpu().numpy().view(np.uint16), oxe)),
                   "out_bitexact": bool(np.array_equal(out.cpu().numpy().view(np.uint16), oout))}
     ms.moe_shuffle_plan_destroy(p)
+    if masked:
+        torch.cuda.synchronize()
+        hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+        for h in masked:
+            hip.hipStreamDestroy(h)
     value = B["total"] / (pipe_ms * 1e-3) / 1e9
     rec = {"metric": "pipelined forward shuffle effective HBM GB/s (fraction of peak), 1 GPU",
            "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(pipe_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16", "data": "synthetic",
            "config": {"workload": cfg.name, "T": T, "H": H, "E": E, "k": k, "R": R, "N": N, "path": "pipelined",
-                      "token_chunks": bounds},
+                      "token_chunks": bounds, "cu_split": cu_split},
            "frac_of_peak": round(value / PEAK_HBM_GBPS, 4), "sequential_ms_per_step": round(seq_ms, 4),
            "speedup_vs_sequential": round(seq_ms / pipe_ms, 4), "algorithmic_bytes": B, "parity": parity,
            "roofline": None, "cpu_baseline": None, "kernel_src_sha256_16": source_digest()}
@@ -933,6 +970,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--chunks", type=int, default=4, help="token chunks for --path pipelined")
+    ap.add_argument("--cu-split", type=float, default=0.0,
+                    help="--path pipelined: run dispatch and combine on CU-masked streams, this fraction of the "
+                         "CUs for dispatch (0: two ordinary streams)")
     ap.add_argument("--path", default="forward",
                     choices=("forward", "backward", "rank-partial", "rank-partial-f32", "pipelined"),
                     help="forward (default): plan + dispatch + combine; backward: combine and dispatch backward; "

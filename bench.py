@@ -184,6 +184,8 @@ def pmc_summary(args):
     import collections
 
     import synth
+    if not args.commands:
+        raise SystemExit("--pmc-summary needs --commands (the rocprofv3 lines that wrote the CSVs, and this one)")
     cfg = synth.CONFIGS[args.config]
     T, H, E, k, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.R
     idx, _ = synth.make_routing(cfg, args.seed)

@@ -56,7 +56,14 @@ def test_counter_summary_scales_by_the_copy_kernel(tmp_path):
                         "--src-sha", "0123456789abcdef", "--fetch-csv", str(tmp_path / "fetch.csv"),
                         "--write-csv", str(tmp_path / "write.csv"), "--trace-stats", str(tmp_path / "stats.csv"),
                         "--out-dir", str(out)], capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0 and "--commands" in r.stderr, "a summary without its commands is refused"
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--pmc-summary", "--config", "0",
+                        "--src-sha", "0123456789abcdef", "--fetch-csv", str(tmp_path / "fetch.csv"),
+                        "--write-csv", str(tmp_path / "write.csv"), "--trace-stats", str(tmp_path / "stats.csv"),
+                        "--out-dir", str(out), "--commands", "rocprofv3 --pmc FETCH_SIZE ..."],
+                       capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
+    assert "    rocprofv3 --pmc FETCH_SIZE ..." in (out / f"kernels_{cfg.name}.md").read_text()
     rec = json.load(open(out / f"traffic_dispatch_fanout_kernel_{cfg.name}.json"))
     assert rec["fetch_scale"] == pytest.approx(2.0)
     assert rec["write_scale"] == pytest.approx(1.0)
@@ -102,7 +109,8 @@ def test_path_counter_summary_sums_the_kernels_of_each_call(tmp_path, monkeypatc
                         "--config", "0", "--src-sha", bench.source_digest(),
                         "--fetch-csv", str(tmp_path / "fetch.csv"),
                         "--write-csv", str(tmp_path / "write.csv"), "--trace-stats", str(tmp_path / "stats.csv"),
-                        "--out-dir", str(out)], capture_output=True, text=True, timeout=300)
+                        "--out-dir", str(out), "--commands", "rocprofv3 ..."],
+                       capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
     text = open(out / f"kernels_backward_{cfg.name}.md").read()
     calls = {ln.split("|")[1].strip(): ln.split("|") for ln in text.splitlines()

@@ -53,12 +53,13 @@ template <int U, bool FULL, int PART>
 __device__ __forceinline__ void combine_bwd_rows(int* s_tile, const u32x4* __restrict__ grad_out,
                                                  const u32x4* __restrict__ ye, const float* __restrict__ w,
                                                  const int32_t* __restrict__ comb_row, u32x4* __restrict__ grad_ye,
-                                                 float* __restrict__ dots, int T, int k, RowSplit rs,
+                                                 float* __restrict__ dots, int T, int k, RowSplit rs, GridSpan gs,
                                                  const int32_t* __restrict__ status)
 {
     if (status[0] != MOE_SHUFFLE_OK) return;
+    const int b = span_block(gs);
     int first, count;
-    block_rows<kWavesPerBlock>((int)blockIdx.x * kWavesPerBlock, T, rs, &first, &count);
+    block_rows<kWavesPerBlock>(b * kWavesPerBlock, T, rs, &first, &count);
     if (count <= 0) return;
     int* s_rows = s_tile;
     int* s_w = s_tile + kWavesPerBlock * k;
@@ -69,7 +70,7 @@ __device__ __forceinline__ void combine_bwd_rows(int* s_tile, const u32x4* __res
     __syncthreads();
 
     const int wave = wave_id(), lane = lane_id();
-    const int u = (int)blockIdx.x * kWavesPerBlock + wave;
+    const int u = b * kWavesPerBlock + wave;
     const int t = fdiv(u, rs.div);
     if (t >= T) return;
     const int V = rs.V;
@@ -151,10 +152,11 @@ __device__ __forceinline__ void combine_bwd_rows(int* s_tile, const u32x4* __res
                                                    const u32x4* __restrict__ ye, const float* __restrict__ w,     \
                                                    const int32_t* __restrict__ comb_row,                          \
                                                    u32x4* __restrict__ grad_ye, float* __restrict__ dots, int T,  \
-                                                   int k, RowSplit rs, const int32_t* __restrict__ status)        \
+                                                   int k, RowSplit rs, GridSpan gs,                               \
+                                                   const int32_t* __restrict__ status)                            \
     {                                                                                                             \
         extern __shared__ int s_tile[];                                                                           \
-        combine_bwd_rows<U, FULL, PART>(s_tile, grad_out, ye, w, comb_row, grad_ye, dots, T, k, rs, status);      \
+        combine_bwd_rows<U, FULL, PART>(s_tile, grad_out, ye, w, comb_row, grad_ye, dots, T, k, rs, gs, status);  \
     }
 // grad_ye[comb_row[t][j]] = bf16(w[t][j] * grad_out[t]).
 MS_CBWD_KERNEL(combine_bwd_grad_kernel, 1)
@@ -206,25 +208,26 @@ static hipError_t launch_cbwd_pass(bool grad, const void* grad_out, const void* 
     RowSplit rs;
     if (!make_split(V, U, T, &rs)) return hipErrorInvalidValue;
     *cpr = rs.cpr;
-    const dim3 grid(grid_for((int64_t)T * rs.cpr, kWavesPerBlock));
+    const int64_t blocks = ((int64_t)T * rs.cpr + kWavesPerBlock - 1) / kWavesPerBlock;
     const size_t lds = tile_lds_bytes(k, 2, kWavesPerBlock);
     const u32x4* gp = (const u32x4*)grad_out;
     const u32x4* yp = (const u32x4*)ye;
     u32x4* gyp = (u32x4*)grad_ye;
     const bool full = V % (kWave * U) == 0;
-    if (grad && full)
-        hipLaunchKernelGGL((combine_bwd_grad_kernel<U, true>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
-                           dots, T, k, rs, status);
-    else if (grad)
-        hipLaunchKernelGGL((combine_bwd_grad_kernel<U, false>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
-                           dots, T, k, rs, status);
-    else if (full)
-        hipLaunchKernelGGL((combine_bwd_dot_kernel<U, true>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
-                           dots, T, k, rs, status);
-    else
-        hipLaunchKernelGGL((combine_bwd_dot_kernel<U, false>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row, gyp,
-                           dots, T, k, rs, status);
-    return hipGetLastError();
+    return launch_spans(blocks, kBlock, [&](dim3 grid, GridSpan gs) {
+        if (grad && full)
+            hipLaunchKernelGGL((combine_bwd_grad_kernel<U, true>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row,
+                               gyp, dots, T, k, rs, gs, status);
+        else if (grad)
+            hipLaunchKernelGGL((combine_bwd_grad_kernel<U, false>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row,
+                               gyp, dots, T, k, rs, gs, status);
+        else if (full)
+            hipLaunchKernelGGL((combine_bwd_dot_kernel<U, true>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row,
+                               gyp, dots, T, k, rs, gs, status);
+        else
+            hipLaunchKernelGGL((combine_bwd_dot_kernel<U, false>), grid, dim3(kBlock), lds, s, gp, yp, w, comb_row,
+                               gyp, dots, T, k, rs, gs, status);
+    });
 }
 
 static hipError_t launch_cbwd(bool grad, int U, const void* grad_out, const void* ye, const float* w,

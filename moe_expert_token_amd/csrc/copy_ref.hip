@@ -9,9 +9,9 @@
 namespace ms {
 
 __global__ __launch_bounds__(kBlock) void copy_reference_kernel(const u32x4* __restrict__ src,
-                                                                u32x4* __restrict__ dst, int64_t n)
+                                                                u32x4* __restrict__ dst, int64_t n, GridSpan gs)
 {
-    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int64_t i = (int64_t)span_block(gs) * kBlock + threadIdx.x;
     if (i < n) store_row16<true>(load_row16<true>(src + i), dst + i);
 }
 
@@ -20,9 +20,10 @@ hipError_t launch_copy_reference(const void* src, void* dst, int64_t n_vectors, 
     if (n_vectors <= 0) return hipSuccess;
     const int64_t blocks = (n_vectors + kBlock - 1) / kBlock;
     if (blocks > 0x7fffffffll) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(copy_reference_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s, (const u32x4*)src,
-                       (u32x4*)dst, n_vectors);
-    return hipGetLastError();
+    return launch_spans(blocks, kBlock, [&](dim3 grid, GridSpan gs) {
+        hipLaunchKernelGGL(copy_reference_kernel, grid, dim3(kBlock), 0, s, (const u32x4*)src, (u32x4*)dst,
+                           n_vectors, gs);
+    });
 }
 
 }  // namespace ms

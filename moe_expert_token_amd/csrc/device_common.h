@@ -177,6 +177,31 @@ struct RowSplit {
     FastDiv div;  // unit -> row
 };
 
+// A grid larger than one dispatch can carry (at most 2^32 - 1 work-items
+// per dimension) goes out as several launches over consecutive pieces of
+// it: block base + blockIdx.x of `total` is the block a kernel works as.
+struct GridSpan {
+    int base, total;
+};
+
+__device__ __forceinline__ int span_block(const GridSpan& g) { return g.base + (int)blockIdx.x; }
+
+// Calls launch(grid, span) for consecutive pieces of `total` blocks of
+// `threads` work-items each, none above 2^32 - 1 work-items; stops at the
+// first launch error.
+template <class F>
+static hipError_t launch_spans(int64_t total, int threads, F&& launch)
+{
+    const int64_t cap = (int64_t)0xFFFFFFFFu / threads;
+    for (int64_t base = 0; base < total; base += cap) {
+        const int64_t n = total - base < cap ? total - base : cap;
+        launch(dim3((unsigned)n), GridSpan{(int)base, (int)total});
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // First unit of this block.  When the row count is known only on the device
 // the grid is sized by a bound and the blocks past the count have nothing to
 // do; those kernels take the units in reverse block order, so the empty
@@ -185,9 +210,9 @@ struct RowSplit {
 // workload 537 -> 526 us, long prefill 1383 -> 1328 us; a grid sized by the
 // exact count would be 479 and 1295 us, which needs a host sync).
 template <int WPB>
-__device__ __forceinline__ int block_first_unit(bool reversed)
+__device__ __forceinline__ int block_first_unit(bool reversed, const GridSpan& g)
 {
-    const int b = reversed ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+    const int b = reversed ? g.total - 1 - span_block(g) : span_block(g);
     return b * WPB;
 }
 
@@ -218,8 +243,6 @@ static inline bool make_split(int V, int U, int64_t rows, RowSplit* rs)
 #define MS_BIG_WAVES 4
 #endif
 constexpr int kWavesBig = MS_BIG_WAVES;
-
-static inline unsigned grid_for(int64_t units, int wpb) { return (unsigned)((units + wpb - 1) / wpb); }
 
 static inline size_t tile_lds_bytes(int width, int arrays, int wpb)
 {

@@ -432,6 +432,8 @@ static PlaceArgs place_args(const Layout& L, const PlanPtrs& P, FastDiv epr)
 
 hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)
 {
+    // one 64-lane wave per tile: ntiles * 64 < T + 64 <= 2^31 work-items,
+    // always one dispatch
     const int ntiles = L.ntiles;
     const size_t lds_count = sizeof(unsigned long long) * L.C;
     const FastDiv epr = make_fastdiv(L.Epr);

@@ -193,7 +193,7 @@ template <int U, bool FULL, int WMODE, bool NTL, bool NTS, int WPB, int MAXW, in
 __device__ __forceinline__ void reduce_rows(int* s_tile, const u32x4* __restrict__ src,
                                             const int32_t* __restrict__ map, int width,
                                             const float* __restrict__ w, u32x4* __restrict__ out, int64_t n_bound,
-                                            const int32_t* __restrict__ n_dev, RowSplit rs,
+                                            const int32_t* __restrict__ n_dev, RowSplit rs, GridSpan gs,
                                             const int32_t* __restrict__ status)
 {
     if (status[0] != MOE_SHUFFLE_OK) return;
@@ -203,8 +203,8 @@ __device__ __forceinline__ void reduce_rows(int* s_tile, const u32x4* __restrict
     int* s_w = s_tile + WPB * width;  // per-slot gates, same shape
 #pragma unroll 1
     for (int round = 0; round < L; ++round) {
-        const int u0 = L == 1 ? block_first_unit<WPB>(n_dev != nullptr)
-                              : (round * (int)gridDim.x + (int)blockIdx.x) * WPB;
+        const int u0 = L == 1 ? block_first_unit<WPB>(n_dev != nullptr, gs)
+                              : (round * gs.total + span_block(gs)) * WPB;
         if (L > 1 && (int64_t)u0 >= n * rs.cpr) return;  // uniform: every later round is empty too
         int first, count;
         block_rows<WPB>(u0, n, rs, &first, &count);
@@ -230,11 +230,12 @@ __device__ __forceinline__ void reduce_rows(int* s_tile, const u32x4* __restrict
                                                         const int32_t* __restrict__ map, int width,             \
                                                         const float* __restrict__ w, u32x4* __restrict__ out,   \
                                                         int64_t n_bound, const int32_t* __restrict__ n_dev,     \
-                                                        RowSplit rs, const int32_t* __restrict__ status)        \
+                                                        RowSplit rs, GridSpan gs,                               \
+                                                        const int32_t* __restrict__ status)                     \
     {                                                                                                            \
         extern __shared__ int s_tile[];                                                                          \
         reduce_rows<U, FULL, WMODE, NTL, NTS, WPB, MAXW, L, IO>(s_tile, src, map, width, w, out, n_bound, n_dev, \
-                                                                rs, status);                                     \
+                                                                rs, gs, status);                                 \
     }
 // ye (expert-major) -> out (token-major): the forward combine.
 MS_REDUCE_KERNEL(combine_rows_kernel, MS_COMBINE_NT_LOAD, MS_COMBINE_NT_STORE)
@@ -312,27 +313,29 @@ enum ReduceKind { kCombine = 0, kSumExpertRows = 1, kSumRankRows = 2 };
 #endif
 
 template <int KIND, int U, bool FULL, int WMODE, int WPB, int MAXW, int L, int IO>
-static void launch_reduce_kernel(dim3 grid, size_t lds, hipStream_t s, const u32x4* src, const int32_t* map,
-                                 int width, const float* w, u32x4* out, int64_t n_bound, const int32_t* n_dev,
-                                 RowSplit rs, const int32_t* status)
+static hipError_t launch_reduce_kernel(int64_t blocks, size_t lds, hipStream_t s, const u32x4* src,
+                                       const int32_t* map, int width, const float* w, u32x4* out, int64_t n_bound,
+                                       const int32_t* n_dev, RowSplit rs, const int32_t* status)
 {
     const dim3 block(WPB * kWave);
-    if constexpr (KIND == kCombine)
-        hipLaunchKernelGGL((combine_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1, IO_BF16>), grid, block, lds, s, src, map,
-                           width, w, out, n_bound, n_dev, rs, status);
-    else if constexpr (KIND == kSumExpertRows && L > 1) {
-        if (n_dev)
-            hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW, L, IO>), grid, block, lds, s, src,
-                               map, width, w, out, n_bound, n_dev, rs, status);
-        else
+    return launch_spans(blocks, WPB * kWave, [&](dim3 grid, GridSpan gs) {
+        if constexpr (KIND == kCombine)
+            hipLaunchKernelGGL((combine_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1, IO_BF16>), grid, block, lds, s, src,
+                               map, width, w, out, n_bound, n_dev, rs, gs, status);
+        else if constexpr (KIND == kSumExpertRows && L > 1) {
+            if (n_dev)
+                hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW, L, IO>), grid, block, lds, s,
+                                   src, map, width, w, out, n_bound, n_dev, rs, gs, status);
+            else
+                hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1, IO>), grid, block, lds, s,
+                                   src, map, width, w, out, n_bound, n_dev, rs, gs, status);
+        } else if constexpr (KIND == kSumExpertRows)
             hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1, IO>), grid, block, lds, s, src,
-                               map, width, w, out, n_bound, n_dev, rs, status);
-    } else if constexpr (KIND == kSumExpertRows)
-        hipLaunchKernelGGL((sum_expert_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1, IO>), grid, block, lds, s, src, map,
-                           width, w, out, n_bound, n_dev, rs, status);
-    else
-        hipLaunchKernelGGL((sum_rank_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1, IO>), grid, block, lds, s, src, map,
-                           width, w, out, n_bound, n_dev, rs, status);
+                               map, width, w, out, n_bound, n_dev, rs, gs, status);
+        else
+            hipLaunchKernelGGL((sum_rank_rows_kernel<U, FULL, WMODE, WPB, MAXW, 1, IO>), grid, block, lds, s, src,
+                               map, width, w, out, n_bound, n_dev, rs, gs, status);
+    });
 }
 
 template <int KIND, int WMODE, int U, int WPB, int IO>
@@ -345,24 +348,22 @@ static hipError_t launch_reduce_uw(const void* src, const int32_t* map, int widt
     constexpr int L = KIND == kSumExpertRows ? MS_SUMX_ROUNDS : 1;
     const int64_t ublocks = (n_bound * rs.cpr + WPB - 1) / WPB;
     const int rounds = n_dev ? L : 1;
-    const dim3 grid((unsigned)((ublocks + rounds - 1) / rounds));
+    const int64_t blocks = (ublocks + rounds - 1) / rounds;
     const size_t lds = tile_lds_bytes(width, 2, WPB);
     const u32x4* sp = (const u32x4*)src;
     u32x4* op = (u32x4*)out;
     const bool full = V % (kWave * U) == 0;
     if (width <= 8 && full)
-        launch_reduce_kernel<KIND, U, true, WMODE, WPB, 8, L, IO>(grid, lds, s, sp, map, width, w, op, n_bound, n_dev,
-                                                                  rs, status);
-    else if (width <= 8)
-        launch_reduce_kernel<KIND, U, false, WMODE, WPB, 8, L, IO>(grid, lds, s, sp, map, width, w, op, n_bound,
-                                                                   n_dev, rs, status);
-    else if (full)
-        launch_reduce_kernel<KIND, U, true, WMODE, WPB, kMaxTopK, L, IO>(grid, lds, s, sp, map, width, w, op, n_bound,
-                                                                         n_dev, rs, status);
-    else
-        launch_reduce_kernel<KIND, U, false, WMODE, WPB, kMaxTopK, L, IO>(grid, lds, s, sp, map, width, w, op,
+        return launch_reduce_kernel<KIND, U, true, WMODE, WPB, 8, L, IO>(blocks, lds, s, sp, map, width, w, op,
+                                                                         n_bound, n_dev, rs, status);
+    if (width <= 8)
+        return launch_reduce_kernel<KIND, U, false, WMODE, WPB, 8, L, IO>(blocks, lds, s, sp, map, width, w, op,
                                                                           n_bound, n_dev, rs, status);
-    return hipGetLastError();
+    if (full)
+        return launch_reduce_kernel<KIND, U, true, WMODE, WPB, kMaxTopK, L, IO>(blocks, lds, s, sp, map, width, w, op,
+                                                                                n_bound, n_dev, rs, status);
+    return launch_reduce_kernel<KIND, U, false, WMODE, WPB, kMaxTopK, L, IO>(blocks, lds, s, sp, map, width, w, op,
+                                                                             n_bound, n_dev, rs, status);
 }
 
 template <int KIND, int WMODE, int U, int IO>

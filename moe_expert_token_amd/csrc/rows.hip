@@ -16,13 +16,13 @@ namespace ms {
 // Body shared by the send and fan-out kernels (two names, so that traces and
 // counters tell the two halves of dispatch apart).  WPB waves per block.
 // With the row count on the device and L > 1, each block takes L rounds of
-// WPB units, round i at unit block i * gridDim.x + blockIdx.x, so the grid
-// sized by the bound has L times fewer blocks and the rounds past the true
-// count end the block at once.
+// WPB units, round i at unit block i * (blocks of the grid) + this block,
+// so the grid sized by the bound has L times fewer blocks and the rounds
+// past the true count end the block at once.
 template <int U, bool FULL, bool NTL, bool NTS, int WPB, int L>
 __device__ __forceinline__ void fanout_rows(int* s_tile, const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                             const int32_t* __restrict__ map, int width, int64_t n_bound,
-                                            const int32_t* __restrict__ n_dev, RowSplit rs,
+                                            const int32_t* __restrict__ n_dev, RowSplit rs, GridSpan gs,
                                             const int32_t* __restrict__ status)
 {
     if (status[0] != MOE_SHUFFLE_OK) return;
@@ -31,8 +31,8 @@ __device__ __forceinline__ void fanout_rows(int* s_tile, const u32x4* __restrict
     const int V = rs.V;
 #pragma unroll 1
     for (int round = 0; round < L; ++round) {
-        const int u0 = L == 1 ? block_first_unit<WPB>(n_dev != nullptr)
-                              : (round * (int)gridDim.x + (int)blockIdx.x) * WPB;
+        const int u0 = L == 1 ? block_first_unit<WPB>(n_dev != nullptr, gs)
+                              : (round * gs.total + span_block(gs)) * WPB;
         if (L > 1 && (int64_t)u0 >= n * rs.cpr) return;  // uniform: every later round is empty too
         int first, count;
         block_rows<WPB>(u0, n, rs, &first, &count);
@@ -68,10 +68,11 @@ __device__ __forceinline__ void fanout_rows(int* s_tile, const u32x4* __restrict
     __global__ __launch_bounds__(WPB * kWave) void NAME(const u32x4* __restrict__ src, u32x4* __restrict__ dst,  \
                                                         const int32_t* __restrict__ map, int width,             \
                                                         int64_t n_bound, const int32_t* __restrict__ n_dev,     \
-                                                        RowSplit rs, const int32_t* __restrict__ status)        \
+                                                        RowSplit rs, GridSpan gs,                               \
+                                                        const int32_t* __restrict__ status)                     \
     {                                                                                                            \
         extern __shared__ int s_tile[]; /* [rows of this block][width] */                                        \
-        fanout_rows<U, FULL, NTL, NTS, WPB, L>(s_tile, src, dst, map, width, n_bound, n_dev, rs, status);        \
+        fanout_rows<U, FULL, NTL, NTS, WPB, L>(s_tile, src, dst, map, width, n_bound, n_dev, rs, gs, status);    \
     }
 // x -> xr: source rows are tokens, targets their rank rows.
 MS_FANOUT_KERNEL(dispatch_send_kernel, MS_SEND_NT_LOAD, MS_SEND_NT_STORE)
@@ -103,24 +104,25 @@ static hipError_t launch_fanout_uwl(bool send, const void* src, void* dst, const
     RowSplit rs;
     if (!make_split(V, U, n_bound, &rs)) return hipErrorInvalidValue;
     const int64_t ublocks = (n_bound * rs.cpr + WPB - 1) / WPB;
-    const dim3 grid((unsigned)((ublocks + L - 1) / L)), block(WPB * kWave);
+    const dim3 block(WPB * kWave);
     const size_t lds = tile_lds_bytes(width, 1, WPB);
     const u32x4* sp = (const u32x4*)src;
     u32x4* dp = (u32x4*)dst;
     const bool full = V % (kWave * U) == 0;
-    if (send && full)
-        hipLaunchKernelGGL((dispatch_send_kernel<U, true, WPB, L>), grid, block, lds, s, sp, dp, map, width, n_bound,
-                           n_dev, rs, status);
-    else if (send)
-        hipLaunchKernelGGL((dispatch_send_kernel<U, false, WPB, L>), grid, block, lds, s, sp, dp, map, width,
-                           n_bound, n_dev, rs, status);
-    else if (full)
-        hipLaunchKernelGGL((dispatch_fanout_kernel<U, true, WPB, L>), grid, block, lds, s, sp, dp, map, width,
-                           n_bound, n_dev, rs, status);
-    else
-        hipLaunchKernelGGL((dispatch_fanout_kernel<U, false, WPB, L>), grid, block, lds, s, sp, dp, map, width,
-                           n_bound, n_dev, rs, status);
-    return hipGetLastError();
+    return launch_spans((ublocks + L - 1) / L, WPB * kWave, [&](dim3 grid, GridSpan gs) {
+        if (send && full)
+            hipLaunchKernelGGL((dispatch_send_kernel<U, true, WPB, L>), grid, block, lds, s, sp, dp, map, width,
+                               n_bound, n_dev, rs, gs, status);
+        else if (send)
+            hipLaunchKernelGGL((dispatch_send_kernel<U, false, WPB, L>), grid, block, lds, s, sp, dp, map, width,
+                               n_bound, n_dev, rs, gs, status);
+        else if (full)
+            hipLaunchKernelGGL((dispatch_fanout_kernel<U, true, WPB, L>), grid, block, lds, s, sp, dp, map, width,
+                               n_bound, n_dev, rs, gs, status);
+        else
+            hipLaunchKernelGGL((dispatch_fanout_kernel<U, false, WPB, L>), grid, block, lds, s, sp, dp, map, width,
+                               n_bound, n_dev, rs, gs, status);
+    });
 }
 
 template <int U, int WPB>
@@ -186,7 +188,7 @@ template <int U, bool FULL, int L>
 __global__ __launch_bounds__(kBlock) void dispatch_fanout_range_kernel(const u32x4* __restrict__ src,
                                                                        u32x4* __restrict__ dst,
                                                                        const int32_t* __restrict__ fan_dst, int D,
-                                                                       RangeArgs g, RowSplit rs,
+                                                                       RangeArgs g, RowSplit rs, GridSpan gs,
                                                                        const int32_t* __restrict__ status)
 {
     extern __shared__ int s_tab[];  // start[R] then exclusive prefix of lengths [R + 1]
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_fanout_range_kernel(const u32
     const int V = rs.V;
 #pragma unroll 1
     for (int round = 0; round < L; ++round) {
-        const int u = (round * (int)gridDim.x + (int)blockIdx.x) * kWavesPerBlock + wave;
+        const int u = (round * gs.total + span_block(gs)) * kWavesPerBlock + wave;
         const int l = fdiv(u, rs.div);
         if (l >= carry) return;  // later rounds only go further
         int lo = 0, hi = R - 1;  // largest r with s_pre[r] <= l
@@ -271,17 +273,17 @@ hipError_t launch_fanout_range(const void* xr, void* xe, const int32_t* fan_dst,
     g.tile1 = t1 == T ? -1 : t1 / kPlanTile;
     constexpr int L = MS_RANGE_ROUNDS;
     const int64_t ublocks = (bound * rs.cpr + kWavesPerBlock - 1) / kWavesPerBlock;
-    const dim3 grid((unsigned)((ublocks + L - 1) / L));
     const size_t lds = sizeof(int) * (2 * (size_t)R + 1);
     const u32x4* sp = (const u32x4*)xr;
     u32x4* dp = (u32x4*)xe;
-    if (V % kWave == 0)
-        hipLaunchKernelGGL((dispatch_fanout_range_kernel<1, true, L>), grid, dim3(kBlock), lds, s, sp, dp, fan_dst, D,
-                           g, rs, status);
-    else
-        hipLaunchKernelGGL((dispatch_fanout_range_kernel<1, false, L>), grid, dim3(kBlock), lds, s, sp, dp, fan_dst,
-                           D, g, rs, status);
-    return hipGetLastError();
+    return launch_spans((ublocks + L - 1) / L, kBlock, [&](dim3 grid, GridSpan gs) {
+        if (V % kWave == 0)
+            hipLaunchKernelGGL((dispatch_fanout_range_kernel<1, true, L>), grid, dim3(kBlock), lds, s, sp, dp,
+                               fan_dst, D, g, rs, gs, status);
+        else
+            hipLaunchKernelGGL((dispatch_fanout_range_kernel<1, false, L>), grid, dim3(kBlock), lds, s, sp, dp,
+                               fan_dst, D, g, rs, gs, status);
+    });
 }
 
 }  // namespace ms

@@ -278,3 +278,61 @@ def test_largest_batch_against_oracle_plan_and_properties():
         assert torch.equal(xe[q0:q1], x[tok_of_q[q0:q1]]), f"xe rows {q0}..{q1}"
     assert torch.equal(out, torch.where(x == -32768, torch.zeros_like(x), x)), "round trip"
     ms.moe_shuffle_plan_destroy(plan)
+
+
+def test_row_count_at_the_int32_limit_closed_form():
+    """The largest batch the index limit admits: H = 8 (one 16-byte vector
+    per row), E = R = 8 and k = 8, so every token reaches every rank and
+    rank r's segment is the tokens in order, r * T + t; with T = 2^28 - 69
+    the fan-out has T * k = 2^31 - 552 units, within 512 of the int32 unit
+    limit (T * k * ceil(H / 512) + 64 < 2^31).  The plan is the definition
+    written out for this case (rows ascending by token inside every
+    segment), the row buffers are x repeated, and with gates 1/8 the
+    combine returns x exactly (-0 read as +0).  About 144 GiB of device
+    memory; everything is checked on the device in slices."""
+    import torch
+    import moe_expert_token_amd as ms
+    T, H, E, k, R = (1 << 28) - 69, 8, 8, 8, 8
+    assert (1 << 31) - 1024 < T * k + 64 < (1 << 31)  # at the limit the host check enforces
+    dev = torch.device("cuda:0")
+    dims = ms.dims_of(T, H, E, k, R)
+    ws = torch.empty(ms.moe_shuffle_workspace_size(dims), dtype=torch.uint8, device=dev)
+    t_all = torch.arange(T, dtype=torch.int32, device=dev)
+    # token t names experts (t + j) mod 8, j = 0..7: distinct in every row
+    idx = ((t_all[:, None] + torch.arange(k, dtype=torch.int32, device=dev)[None, :]) % E).contiguous()
+    w = torch.full((T, k), 0.125, dtype=torch.float32, device=dev)
+    gen = torch.Generator(device="cuda").manual_seed(31)
+    x = torch.randn((T, H), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+    xr = torch.empty((T * R, H), dtype=torch.int16, device=dev)
+    xe = torch.empty((T * k, H), dtype=torch.int16, device=dev)
+    out = torch.empty((T, H), dtype=torch.int16, device=dev)
+    h = harness()
+    h.say(f"[int32-limit] T={T} H={H} E={E} k={k} R={R}: plan, dispatch, combine")
+    plan = ms.moe_shuffle_plan(dims, idx, ws)
+    ms.moe_shuffle_dispatch(plan, x, xr, xe)
+    ms.moe_shuffle_combine(plan, xe, w, out)
+    assert ms.moe_shuffle_plan_query(plan)["N"] == T * R
+    v = ms.plan_array_views(plan, T * R)
+    seg = torch.arange(R + 1, dtype=torch.int64, device=dev) * T
+    assert torch.equal(v["rank_offset"].long(), seg) and torch.equal(v["expert_offset"].long(), seg)
+    step = 1 << 25
+    for t0 in range(0, T, step):
+        t1 = min(T, t0 + step)
+        tt = t_all[t0:t1]
+        rows = tt[:, None].long() + seg[None, :R]                  # rank (= expert) r's row of token t
+        assert torch.equal(v["tok_rank_row"][t0:t1].long(), rows), f"tok_rank_row {t0}"
+        assert torch.equal(v["comb_row"][t0:t1].long(), idx[t0:t1].long() * T + tt[:, None].long()), \
+            f"comb_row {t0}"
+        ref = torch.where(x[t0:t1] == -32768, torch.zeros_like(x[t0:t1]), x[t0:t1])
+        assert torch.equal(out[t0:t1], ref), f"out {t0}"
+        for r in range(R):
+            p0 = r * T
+            assert torch.equal(v["send_token"][p0 + t0:p0 + t1], tt), f"send_token rank {r} at {t0}"
+            assert torch.equal(v["fan_src"][p0 + t0:p0 + t1].long(), tt.long() + p0), f"fan_src {r} at {t0}"
+            assert torch.equal(xr[p0 + t0:p0 + t1], x[t0:t1]), f"xr rank {r} at {t0}"
+            assert torch.equal(xe[p0 + t0:p0 + t1], x[t0:t1]), f"xe expert {r} at {t0}"
+    ms.moe_shuffle_plan_destroy(plan)
+    h.say("[int32-limit] plan, xr, xe and out as the closed form gives")
+    del ws, idx, w, x, xr, xe, out, t_all, v
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()

@@ -288,7 +288,8 @@ def test_row_count_at_the_int32_limit_closed_form():
     limit (T * k * ceil(H / 512) + 64 < 2^31).  The plan is the definition
     written out for this case (rows ascending by token inside every
     segment), the row buffers are x repeated, and with gates 1/8 the
-    combine returns x exactly (-0 read as +0).  About 144 GiB of device
+    combine returns x exactly (-0 read as +0); the training direction on
+    the same plan has a closed form too (below).  About 185 GiB of device
     memory; everything is checked on the device in slices."""
     import torch
     import moe_expert_token_amd as ms
@@ -331,8 +332,36 @@ def test_row_count_at_the_int32_limit_closed_form():
             assert torch.equal(v["fan_src"][p0 + t0:p0 + t1].long(), tt.long() + p0), f"fan_src {r} at {t0}"
             assert torch.equal(xr[p0 + t0:p0 + t1], x[t0:t1]), f"xr rank {r} at {t0}"
             assert torch.equal(xe[p0 + t0:p0 + t1], x[t0:t1]), f"xe expert {r} at {t0}"
+    h.say("[int32-limit] plan, xr, xe and out as the closed form gives; now the training direction")
+
+    # Training direction on the same plan, with xe (x[t] in all 8 expert
+    # rows of t) as both grad_xe and ye and x as grad_out: the receiver sum
+    # of a rank row is its one expert row (x[t]), the sender sum of token t
+    # is 8 x[t] (exact), grad_ye = bf16(x[t] / 8) (exact) and grad_w[t][j]
+    # = sum_h x[t][h]^2 summed in fp32.
+    xr.fill_(0x7F7F)
+    out.fill_(0x7F7F)
+    ms.moe_shuffle_dispatch_backward(plan, xe, xr, out)
+    gye = torch.empty((T * k, H), dtype=torch.int16, device=dev)
+    gw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ms.moe_shuffle_combine_backward(plan, x, xe, w, gye, gw)
+    torch.cuda.synchronize()
+    for t0 in range(0, T, step):
+        t1 = min(T, t0 + step)
+        xs = x[t0:t1]
+        x0 = torch.where(xs == -32768, torch.zeros_like(xs), xs)   # fma(1, -0, +0) = +0
+        xf = xs.view(torch.bfloat16).float()
+        eight = torch.where(xs == -32768, torch.zeros_like(xs), (xf * 8).to(torch.bfloat16).view(torch.int16))
+        eighth = (xf * 0.125).to(torch.bfloat16).view(torch.int16)
+        assert torch.equal(out[t0:t1], eight), f"grad_x {t0}"
+        ss = (xf.double() ** 2).sum(1, keepdim=True)
+        assert bool(((gw[t0:t1].double() - ss).abs() <= 1e-6 * ss + 1e-30).all()), f"grad_w {t0}"
+        for r in range(R):
+            p0 = r * T
+            assert torch.equal(xr[p0 + t0:p0 + t1], x0), f"grad_xr rank {r} at {t0}"
+            assert torch.equal(gye[p0 + t0:p0 + t1], eighth), f"grad_ye expert {r} at {t0}"
     ms.moe_shuffle_plan_destroy(plan)
-    h.say("[int32-limit] plan, xr, xe and out as the closed form gives")
-    del ws, idx, w, x, xr, xe, out, t_all, v
+    h.say("[int32-limit] grad_xr, grad_x, grad_ye and grad_w as the closed form gives")
+    del ws, idx, w, x, xr, xe, out, t_all, v, gye, gw
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -360,8 +360,28 @@ def test_row_count_at_the_int32_limit_closed_form():
             p0 = r * T
             assert torch.equal(xr[p0 + t0:p0 + t1], x0), f"grad_xr rank {r} at {t0}"
             assert torch.equal(gye[p0 + t0:p0 + t1], eighth), f"grad_ye expert {r} at {t0}"
+    h.say("[int32-limit] grad_xr, grad_x, grad_ye and grad_w as the closed form gives; now two token ranges")
+
+    # The token-range calls over [0, cut) and [cut, T) give the forward
+    # closed form again.
+    del gye, gw
+    cut = (T // 128) * 64
+    for buf in (xr, xe, out):
+        buf.fill_(0x7F7F)
+    for t0, t1 in ((0, cut), (cut, T)):
+        ms.moe_shuffle_dispatch_range(plan, x, xr, xe, t0, t1)
+        ms.moe_shuffle_combine_range(plan, xe, w, out, t0, t1)
+    torch.cuda.synchronize()
+    for t0 in range(0, T, step):
+        t1 = min(T, t0 + step)
+        ref = torch.where(x[t0:t1] == -32768, torch.zeros_like(x[t0:t1]), x[t0:t1])
+        assert torch.equal(out[t0:t1], ref), f"range out {t0}"
+        for r in range(R):
+            p0 = r * T
+            assert torch.equal(xr[p0 + t0:p0 + t1], x[t0:t1]), f"range xr rank {r} at {t0}"
+            assert torch.equal(xe[p0 + t0:p0 + t1], x[t0:t1]), f"range xe expert {r} at {t0}"
     ms.moe_shuffle_plan_destroy(plan)
-    h.say("[int32-limit] grad_xr, grad_x, grad_ye and grad_w as the closed form gives")
-    del ws, idx, w, x, xr, xe, out, t_all, v, gye, gw
+    h.say("[int32-limit] token ranges as the closed form gives")
+    del ws, idx, w, x, xr, xe, out, t_all, v
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -289,8 +289,9 @@ def test_row_count_at_the_int32_limit_closed_form():
     written out for this case (rows ascending by token inside every
     segment), the row buffers are x repeated, and with gates 1/8 the
     combine returns x exactly (-0 read as +0); the training direction on
-    the same plan has a closed form too (below).  About 185 GiB of device
-    memory; everything is checked on the device in slices."""
+    the same plan, the token ranges and the rank-partial combines have
+    closed forms too (below).  About 210 GiB of device memory at the peak;
+    everything is checked on the device in slices."""
     import torch
     import moe_expert_token_amd as ms
     T, H, E, k, R = (1 << 28) - 69, 8, 8, 8, 8
@@ -380,8 +381,35 @@ def test_row_count_at_the_int32_limit_closed_form():
             p0 = r * T
             assert torch.equal(xr[p0 + t0:p0 + t1], x[t0:t1]), f"range xr rank {r} at {t0}"
             assert torch.equal(xe[p0 + t0:p0 + t1], x[t0:t1]), f"range xe expert {r} at {t0}"
+    h.say("[int32-limit] token ranges as the closed form gives; now the rank-partial combines")
+
+    # Rank-partial combine (xe as ye): each rank row's partial is its one
+    # expert row times 1/8, exact in bf16 and in fp32, and out is x again.
+    p32 = torch.empty((T * R, H), dtype=torch.float32, device=dev)
+    for f32 in (False, True):
+        xr.fill_(0x7F7F)
+        out.fill_(0x7F7F)
+        if f32:
+            ms.moe_shuffle_combine_rank_partial_f32(plan, xe, w, p32, out)
+        else:
+            ms.moe_shuffle_combine_rank_partial(plan, xe, w, xr, out)
+        torch.cuda.synchronize()
+        for t0 in range(0, T, step):
+            t1 = min(T, t0 + step)
+            xs = x[t0:t1]
+            ref = torch.where(xs == -32768, torch.zeros_like(xs), xs)
+            assert torch.equal(out[t0:t1], ref), f"rank-partial (fp32 {f32}) out {t0}"
+            eighth = xs.view(torch.bfloat16).float() * 0.125
+            for r in range(R):
+                p0 = r * T
+                if f32:
+                    got = p32[p0 + t0:p0 + t1]
+                    assert torch.equal(got, eighth + 0.0), f"fp32 partial rank {r} at {t0}"  # -0 -> +0
+                else:
+                    want = torch.where(xs == -32768, torch.zeros_like(xs), eighth.to(torch.bfloat16).view(torch.int16))
+                    assert torch.equal(xr[p0 + t0:p0 + t1], want), f"partial rank {r} at {t0}"
     ms.moe_shuffle_plan_destroy(plan)
-    h.say("[int32-limit] token ranges as the closed form gives")
-    del ws, idx, w, x, xr, xe, out, t_all, v
+    h.say("[int32-limit] rank-partial combines as the closed form gives")
+    del ws, idx, w, x, xr, xe, out, t_all, v, p32
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

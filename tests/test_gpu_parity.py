@@ -297,6 +297,9 @@ def test_row_count_at_the_int32_limit_closed_form():
     T, H, E, k, R = (1 << 28) - 69, 8, 8, 8, 8
     assert (1 << 31) - 1024 < T * k + 64 < (1 << 31)  # at the limit the host check enforces
     dev = torch.device("cuda:0")
+    free, _ = torch.cuda.mem_get_info(dev)
+    if free < (215 << 30):
+        pytest.skip(f"needs about 210 GiB of free device memory, {free / 2**30:.0f} GiB free")
     dims = ms.dims_of(T, H, E, k, R)
     ws = torch.empty(ms.moe_shuffle_workspace_size(dims), dtype=torch.uint8, device=dev)
     t_all = torch.arange(T, dtype=torch.int32, device=dev)

@@ -135,3 +135,16 @@ def test_static_plan_argument_errors_on_the_host():
     for cfg in synth.CONFIGS.values():
         assert ms.moe_shuffle_workspace_size(ms.dims_of(cfg.T, cfg.H, cfg.E, cfg.k, cfg.R)) <= \
             ms.STATIC_WORKSPACE_BYTES, cfg.name
+
+
+def test_c_gpu_driver_compiles_cleanly(tmp_path):
+    """The C program the GPU tests drive the library with builds against
+    the header with every warning on and none from its own source."""
+    import subprocess
+    import sys
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import c_driver
+    r = subprocess.run(c_driver.compile_cmd(str(tmp_path / "drive"), extra=("-Wall", "-Wextra")),
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert "abi_gpu_drive.c:" not in r.stderr, r.stderr

@@ -1,5 +1,6 @@
-"""Stream and graph use.  The forward step (plan, dispatch, combine) and the combine backward
-captured once in a HIP graph and replayed: every replay must give the
+"""Stream and graph use.  The forward step (plan, dispatch, combine), the
+combine backward, and the dispatch backward with both rank-partial
+combines, each captured once in a HIP graph and replayed: every replay must give the
 bits of the same calls run eagerly, with eager work and synchronisations
 between the replays.  The library records no memset or host copy in these
 calls, so a captured step is the step."""
@@ -109,6 +110,60 @@ def test_combine_backward_replays_in_a_graph():
         torch.cuda.synchronize()
         assert torch.equal(gye, want_gye), f"replay {replay}: grad_ye"
         assert torch.equal(gw.view(torch.int32), want_gw.view(torch.int32)), f"replay {replay}: grad_w"
+    ms.moe_shuffle_plan_destroy(plan)
+
+
+def test_dispatch_backward_and_rank_partial_replay_in_a_graph():
+    """The receiver and sender sums in all three forms (dispatch backward,
+    rank-partial combine with bf16 and with fp32 partials; the last two
+    include the per-row gate kernel) captured in one graph."""
+    import torch
+    import moe_expert_token_amd as ms
+    import gpu_harness as h
+    T, H, E, k, R = 900, 1032, 48, 6, 8
+    rng = np.random.default_rng(23)
+    idx, w = synth.random_routing(rng, T, E, k, signed_gates=True)
+    dims = ms.dims_of(T, H, E, k, R)
+    ws = torch.empty(ms.moe_shuffle_workspace_size(dims), dtype=torch.uint8, device="cuda")
+    plan = ms.moe_shuffle_plan(dims, torch.from_numpy(idx).cuda(), ws)
+    KR = min(k, R)
+    w_d = torch.from_numpy(w).cuda()
+    src = torch.empty((T * k, H), dtype=torch.int16, device="cuda")
+    bufs = {"grad_xr": torch.empty((T * KR, H), dtype=torch.int16, device="cuda"),
+            "grad_x": torch.empty((T, H), dtype=torch.int16, device="cuda"),
+            "partial": torch.empty((T * KR, H), dtype=torch.int16, device="cuda"),
+            "out": torch.empty((T, H), dtype=torch.int16, device="cuda"),
+            "partial32": torch.empty((T * KR, H), dtype=torch.float32, device="cuda"),
+            "out32": torch.empty((T, H), dtype=torch.int16, device="cuda")}
+
+    def calls():
+        ms.moe_shuffle_dispatch_backward(plan, src, bufs["grad_xr"], bufs["grad_x"])
+        ms.moe_shuffle_combine_rank_partial(plan, src, w_d, bufs["partial"], bufs["out"])
+        ms.moe_shuffle_combine_rank_partial_f32(plan, src, w_d, bufs["partial32"], bufs["out32"])
+
+    N = ms.moe_shuffle_plan_query(plan)["N"]
+    src.copy_(h.to_dev16(synth.wide_bf16(rng, (T * k, H))))
+    calls()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for replay in range(3):
+        src.copy_(h.to_dev16(synth.wide_bf16(rng, (T * k, H))))
+        calls()
+        torch.cuda.synchronize()
+        want = {key: b.clone() for key, b in bufs.items()}
+        for b in bufs.values():
+            b.view(torch.int16).fill_(0x7F7F)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for key, b in bufs.items():
+            rows = N if key in ("grad_xr", "partial", "partial32") else T
+            got, ref = b[:rows], want[key][:rows]
+            if b.dtype == torch.float32:
+                got, ref = got.view(torch.int32), ref.view(torch.int32)
+            assert torch.equal(got, ref), f"replay {replay}: {key}"
     ms.moe_shuffle_plan_destroy(plan)
 
 

@@ -543,7 +543,17 @@ def bench_path(args):
         "cpu_baseline": None, "parity": parity, "kernel_src_sha256_16": source_digest(),
     }
     ms.moe_shuffle_plan_destroy(plan)
-    print(json.dumps(rec), flush=True)
+    return rec
+
+
+def path_summary(rec):
+    """The figures of a --path record, for the per_path object of the forward line."""
+    return {"ms_per_step": rec["ms_per_step"], "GBps": rec["value"], "frac_of_peak": rec["frac_of_peak"],
+            "tokens_per_s": rec["tokens_per_s"], "kernel_us": rec["kernel_us"],
+            "algorithmic_bytes": rec["algorithmic_bytes"]["total"],
+            "roofline": {"kernel": rec["roofline"]["kernel"], "frac": rec["roofline"]["frac"],
+                         "traffic": rec["roofline"]["traffic"]},
+            "parity": rec["parity"]}
 
 
 def bench_pipelined(args):
@@ -967,6 +977,10 @@ def main():
     ap.add_argument("--per-config", default="0,1,2,3,4",
                     help="workloads whose figures go into the per_config object of the forward line "
                          "(comma-separated ids, or none)")
+    ap.add_argument("--per-path", default="auto",
+                    help="other paths whose figures on the same workload go into the per_path object of the "
+                         "forward line (comma-separated, or none; auto: backward, rank-partial and "
+                         "rank-partial-f32 unless --per-config is none)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget-s", type=float, default=12.0, help="CPU-oracle timing budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -1023,7 +1037,7 @@ def main():
         bench_pipelined(args)
         return
     if args.path != "forward":
-        bench_path(args)
+        print(json.dumps(bench_path(args)), flush=True)
         return
 
     head = forward_run(args, args.config, dev, full=True)
@@ -1037,6 +1051,17 @@ def main():
                 per[str(cid)] = config_summary(forward_run(args, cid, dev, full=False,
                                                            ceiling=head["copy_ceiling"]))
         head["per_config"] = per
+    per_path = args.per_path
+    if per_path == "auto":
+        per_path = "none" if args.per_config == "none" else "backward,rank-partial,rank-partial-f32"
+    paths = [p.strip() for p in per_path.split(",") if p.strip()] if per_path != "none" else []
+    if paths:
+        head["per_path"] = {}
+        for p in paths:
+            torch.cuda.empty_cache()
+            sub = argparse.Namespace(**vars(args))
+            sub.path = p
+            head["per_path"][p] = path_summary(bench_path(sub))
     print(json.dumps(head), flush=True)
 
 

@@ -678,7 +678,7 @@ def bench_pipelined(args):
            "frac_of_peak": round(value / PEAK_HBM_GBPS, 4), "sequential_ms_per_step": round(seq_ms, 4),
            "speedup_vs_sequential": round(seq_ms / pipe_ms, 4), "algorithmic_bytes": B, "parity": parity,
            "roofline": None, "cpu_baseline": None, "kernel_src_sha256_16": source_digest()}
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 def forward_run(args, cfg_id, dev, full=True, ceiling=None):
@@ -979,8 +979,8 @@ def main():
                          "(comma-separated ids, or none)")
     ap.add_argument("--per-path", default="auto",
                     help="other paths whose figures on the same workload go into the per_path object of the "
-                         "forward line (comma-separated, or none; auto: backward, rank-partial and "
-                         "rank-partial-f32 unless --per-config is none)")
+                         "forward line (comma-separated, or none; auto: backward, rank-partial, "
+                         "rank-partial-f32 and pipelined unless --per-config is none)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget-s", type=float, default=12.0, help="CPU-oracle timing budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -1034,7 +1034,7 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda:0")
     if args.path == "pipelined":
-        bench_pipelined(args)
+        print(json.dumps(bench_pipelined(args)), flush=True)
         return
     if args.path != "forward":
         print(json.dumps(bench_path(args)), flush=True)
@@ -1053,7 +1053,7 @@ def main():
         head["per_config"] = per
     per_path = args.per_path
     if per_path == "auto":
-        per_path = "none" if args.per_config == "none" else "backward,rank-partial,rank-partial-f32"
+        per_path = "none" if args.per_config == "none" else "backward,rank-partial,rank-partial-f32,pipelined"
     paths = [p.strip() for p in per_path.split(",") if p.strip()] if per_path != "none" else []
     if paths:
         head["per_path"] = {}
@@ -1061,7 +1061,15 @@ def main():
             torch.cuda.empty_cache()
             sub = argparse.Namespace(**vars(args))
             sub.path = p
-            head["per_path"][p] = path_summary(bench_path(sub))
+            if p == "pipelined":
+                rec = bench_pipelined(sub)
+                head["per_path"][p] = {"ms_per_step": rec["ms_per_step"], "GBps": rec["value"],
+                                       "frac_of_peak": rec["frac_of_peak"],
+                                       "sequential_ms_per_step": rec["sequential_ms_per_step"],
+                                       "speedup_vs_sequential": rec["speedup_vs_sequential"],
+                                       "token_chunks": rec["config"]["token_chunks"], "parity": rec["parity"]}
+            else:
+                head["per_path"][p] = path_summary(bench_path(sub))
     print(json.dumps(head), flush=True)
 
 

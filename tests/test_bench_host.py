@@ -203,3 +203,15 @@ def test_occupancy_and_latency_summary_derives_each_figure(tmp_path):
     cells = [c.strip() for c in rows[0].strip("|").split("|")]
     assert cells[0] == "`ms::combine_rows_kernel<1, true, 1, 4, 8, 1, 0>`"
     assert cells[1:] == ["2", "184.0", "0.50", "0.25", "1500", "5.9", "0.75", "0.50", "2000", "4000", "3000"]
+
+
+def test_path_summary_keeps_the_figures_the_forward_line_reports():
+    rec = {"ms_per_step": 0.8, "value": 5800.0, "frac_of_peak": 0.725, "tokens_per_s": 1.0e7,
+           "kernel_us": {"combine_bwd": 365.0}, "algorithmic_bytes": {"total": 4.6e9, "combine_bwd": 2e9},
+           "roofline": {"kernel": "combine_bwd", "frac": 0.68, "traffic": 2.1e9, "peak": 8000.0},
+           "parity": {"grad_x_bitexact": True}, "config": {"T": 8192}}
+    s = bench.path_summary(rec)
+    assert s == {"ms_per_step": 0.8, "GBps": 5800.0, "frac_of_peak": 0.725, "tokens_per_s": 1.0e7,
+                 "kernel_us": {"combine_bwd": 365.0}, "algorithmic_bytes": 4.6e9,
+                 "roofline": {"kernel": "combine_bwd", "frac": 0.68, "traffic": 2.1e9},
+                 "parity": {"grad_x_bitexact": True}}

@@ -366,14 +366,23 @@ static hipError_t launch_reduce_uw(const void* src, const int32_t* map, int widt
                                                                              n_bound, n_dev, rs, status);
 }
 
+// Waves per block of the receiver's sum (its row count is on the device):
+// 2 against 4, measured on whole steps on the MI355X, DeepSeek-V3-like /
+// skewed / long prefill: backward 0.803 / 1.364 / 3.630 against 0.808 /
+// 1.367 / 3.656 ms, rank-partial 0.440 / 0.669 / 2.011 against 0.445 /
+// 0.670 / 2.025 ms (fp32 partials within 0.3 % either way).
+#ifndef MS_SUMX_WAVES
+#define MS_SUMX_WAVES 2
+#endif
+
 template <int KIND, int WMODE, int U, int IO>
 static hipError_t launch_reduce_u(const void* src, const int32_t* map, int width, const float* w, void* out,
                                   int64_t n_bound, const int32_t* n_dev, int V, const int32_t* status, hipStream_t s)
 {
     if constexpr (U <= 2) {
         if (n_dev)
-            return launch_reduce_uw<KIND, WMODE, U, kWavesBig, IO>(src, map, width, w, out, n_bound, n_dev, V, status,
-                                                                   s);
+            return launch_reduce_uw<KIND, WMODE, U, MS_SUMX_WAVES, IO>(src, map, width, w, out, n_bound, n_dev, V,
+                                                                       status, s);
     }
     return launch_reduce_uw<KIND, WMODE, U, kWavesPerBlock, IO>(src, map, width, w, out, n_bound, n_dev, V, status, s);
 }

@@ -374,6 +374,13 @@ static hipError_t launch_reduce_uw(const void* src, const int32_t* map, int widt
 #ifndef MS_SUMX_WAVES
 #define MS_SUMX_WAVES 2
 #endif
+// Waves per block of the sender's sum: 4.  Measured on whole steps on the
+// MI355X, 2 waves were as fast or slower everywhere; 8 waves gained 0.5 %
+// on the DeepSeek-V3-like and skewed workloads and lost 1-2 % on the long
+// prefill.
+#ifndef MS_SUMR_WAVES
+#define MS_SUMR_WAVES kWavesPerBlock
+#endif
 
 template <int KIND, int WMODE, int U, int IO>
 static hipError_t launch_reduce_u(const void* src, const int32_t* map, int width, const float* w, void* out,
@@ -384,6 +391,9 @@ static hipError_t launch_reduce_u(const void* src, const int32_t* map, int width
             return launch_reduce_uw<KIND, WMODE, U, MS_SUMX_WAVES, IO>(src, map, width, w, out, n_bound, n_dev, V,
                                                                        status, s);
     }
+    if constexpr (KIND == kSumRankRows)
+        return launch_reduce_uw<KIND, WMODE, U, MS_SUMR_WAVES, IO>(src, map, width, w, out, n_bound, n_dev, V, status,
+                                                                   s);
     return launch_reduce_uw<KIND, WMODE, U, kWavesPerBlock, IO>(src, map, width, w, out, n_bound, n_dev, V, status, s);
 }
 

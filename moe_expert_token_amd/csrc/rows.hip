@@ -134,6 +134,14 @@ static hipError_t launch_fanout_uw(bool send, const void* src, void* dst, const 
     return launch_fanout_uwl<U, WPB, 1>(send, src, dst, map, width, n_bound, n_dev, V, status, s);
 }
 
+// Waves per block of the send (its row count is known on the host): 2
+// against 4, measured on the MI355X (DeepSeek-V3-like / skewed / long
+// prefill): 146 / 200 / 669 us against 153 / 206 / 715 us; 1, 8 and 16
+// waves were slower.
+#ifndef MS_SEND_WAVES
+#define MS_SEND_WAVES 2
+#endif
+
 template <int U>
 static hipError_t launch_fanout_u(bool send, const void* src, void* dst, const int32_t* map, int width,
                                   int64_t n_bound, const int32_t* n_dev, int V, const int32_t* status, hipStream_t s)
@@ -141,6 +149,7 @@ static hipError_t launch_fanout_u(bool send, const void* src, void* dst, const i
     if constexpr (U <= 2) {  // big blocks only with small units (no register pressure)
         if (n_dev) return launch_fanout_uw<U, kWavesBig>(send, src, dst, map, width, n_bound, n_dev, V, status, s);
     }
+    if (send) return launch_fanout_uw<U, MS_SEND_WAVES>(send, src, dst, map, width, n_bound, n_dev, V, status, s);
     return launch_fanout_uw<U, kWavesPerBlock>(send, src, dst, map, width, n_bound, n_dev, V, status, s);
 }
 

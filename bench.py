@@ -39,6 +39,10 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
 METRIC = "dispatch+combine effective HBM GB/s (fraction of peak) and tokens/s, 1 GPU"
 KERNEL_DIR = os.path.join(ROOT, "moe_expert_token_amd", "csrc")
 KERNEL_SRCS = ("device_common.h", "plan.hip", "rows.hip", "reduce.hip", "combine_bwd.hip", "copy_ref.hip")
+# The files that hold the row kernels (everything but the plan): the stored
+# traffic records cover only kernels defined here, so a change to the plan
+# leaves them valid.
+DATA_KERNEL_SRCS = tuple(n for n in KERNEL_SRCS if n != "plan.hip")
 
 
 def log(*a):
@@ -71,12 +75,17 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def source_digest() -> str:
+def source_digest(names=KERNEL_SRCS) -> str:
     """Hash of the kernel sources (the files that hold device code)."""
     h = hashlib.sha256()
-    for name in KERNEL_SRCS:
+    for name in names:
         h.update(name.encode() + b"\0" + open(os.path.join(KERNEL_DIR, name), "rb").read())
     return h.hexdigest()[:16]
+
+
+def data_source_digest() -> str:
+    """Hash of the row kernels' sources (the plan's excluded)."""
+    return source_digest(DATA_KERNEL_SRCS)
 
 
 KERNEL_NAMES = {"plan": "plan_count/scan/place", "send": "dispatch_send_kernel",
@@ -93,7 +102,7 @@ def load_traffic(workload: str, kernel: str):
         rec = json.load(open(path))
     except ValueError:
         return None
-    if rec.get("kernel_src_sha256_16") != source_digest():
+    if rec.get("data_kernel_src_sha256_16") != data_source_digest():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -108,7 +117,7 @@ def load_path_traffic(workload: str, path: str, calls):
             rec = json.load(open(f))
         except (OSError, ValueError):
             return None
-        if rec.get("kernel_src_sha256_16") != source_digest():
+        if rec.get("data_kernel_src_sha256_16") != data_source_digest():
             return None
         total += rec["hbm_bytes_per_call"]
     return total
@@ -239,6 +248,7 @@ def pmc_summary(args):
         rows.append((base, name.split("(")[0], avg_us, fb, wb, alg))
         if alg is not None:
             rec = {"kernel": base, "workload": cfg.name, "kernel_src_sha256_16": digest,
+                   "data_kernel_src_sha256_16": args.data_src_sha or data_source_digest(),
                    "hbm_bytes_per_launch": round(fb + wb), "fetch_bytes_per_launch": round(fb),
                    "write_bytes_per_launch": round(wb), "alg_bytes_per_launch": alg,
                    "traffic_over_alg": round((fb + wb) / alg, 4),
@@ -388,7 +398,8 @@ def pmc_path_summary(args, cfg, N, fetch, write, f_factor, w_factor, stats, copy
         lines.append(f"| {call} | {', '.join(sorted(v[0] for v in mine))} | {us:.1f} | {fb / 1e6:.1f} | "
                      f"{wb / 1e6:.1f} | {B[call] / 1e6:.1f} | {(fb + wb) / B[call]:.3f} |")
         rec = {"path": args.path, "call": call, "kernels": sorted(v[0] for v in mine), "workload": cfg.name,
-               "kernel_src_sha256_16": digest, "hbm_bytes_per_call": round(fb + wb),
+               "kernel_src_sha256_16": digest, "data_kernel_src_sha256_16": args.data_src_sha or data_source_digest(),
+               "hbm_bytes_per_call": round(fb + wb),
                "fetch_bytes_per_call": round(fb), "write_bytes_per_call": round(wb),
                "alg_bytes_per_call": B[call], "traffic_over_alg": round((fb + wb) / B[call], 4),
                "fetch_scale": round(f_factor, 4), "write_scale": round(w_factor, 4),
@@ -1001,6 +1012,8 @@ def main():
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--commands", nargs="*", default=[])
     ap.add_argument("--src-sha", default=None, help="kernel source hash of the profiled run (default: current)")
+    ap.add_argument("--data-src-sha", default=None,
+                    help="row-kernel source hash of the profiled run (default: current)")
     ap.add_argument("--counter-summary", action="store_true",
                     help="summarise rocprofv3 --pmc CSVs of any counters into profiles/ (no GPU)")
     ap.add_argument("--counter-csv", nargs="*", default=[])

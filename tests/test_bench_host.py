@@ -135,11 +135,25 @@ def test_stored_traffic_is_used_only_for_the_profiled_source(tmp_path, monkeypat
     (tmp_path / "profiles").mkdir()
     path = tmp_path / "profiles" / "traffic_dispatch_fanout_kernel_w.json"
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    json.dump({"kernel_src_sha256_16": bench.source_digest(), "hbm_bytes_per_launch": 1234}, open(path, "w"))
+    json.dump({"data_kernel_src_sha256_16": bench.data_source_digest(), "hbm_bytes_per_launch": 1234},
+              open(path, "w"))
     assert bench.load_traffic("w", "fanout") == 1234
-    json.dump({"kernel_src_sha256_16": "not-this-source", "hbm_bytes_per_launch": 1234}, open(path, "w"))
+    json.dump({"data_kernel_src_sha256_16": "not-this-source", "hbm_bytes_per_launch": 1234}, open(path, "w"))
+    assert bench.load_traffic("w", "fanout") is None
+    # a record stamped with the hash of every source, plan included, is not enough
+    json.dump({"kernel_src_sha256_16": bench.source_digest(), "hbm_bytes_per_launch": 1234}, open(path, "w"))
     assert bench.load_traffic("w", "fanout") is None
     assert bench.load_traffic("absent", "fanout") is None
+
+
+def test_row_kernel_hash_leaves_out_only_the_plan():
+    """The traffic records cover row kernels only; their hash covers every
+    device source except the plan's, so a plan change keeps them valid and a
+    row-kernel change drops them."""
+    assert "plan.hip" in bench.KERNEL_SRCS and "plan.hip" not in bench.DATA_KERNEL_SRCS
+    assert set(bench.KERNEL_SRCS) - set(bench.DATA_KERNEL_SRCS) == {"plan.hip"}
+    assert bench.data_source_digest() == bench.source_digest(bench.DATA_KERNEL_SRCS)
+    assert bench.data_source_digest() != bench.source_digest()
 
 
 def test_algorithmic_bytes_count_each_step_once():

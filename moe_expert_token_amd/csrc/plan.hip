@@ -11,33 +11,70 @@
 //               offsets, and gives every (token, rank) and (token, expert)
 //               pair its row: tile base + mbcnt(mask).  Rows come out in
 //               ascending token order inside every segment.
-//   plan_small  the three steps in one block for a batch of at most 16
-//               tiles (one launch instead of three).
+//   plan_recount  up to 16 tiles with E + R <= 64: one launch of one
+//               block per tile, each block counting every tile again
+//               (ballots over per-lane column masks), so no block waits on
+//               another; then one wave places the block's tile.
+//   plan_small  up to 16 tiles (and 32 tile-slots): the three steps in one
+//               block of one wave per tile.
+// Each form loads a token's ids once, for both its count and place steps.
 #include "device_common.h"
 
 namespace ms {
 
 // ---------------------------------------------------------------- plan_count
 
-// One wave per 64-token tile.  hist is column-major [(C+1)][ntiles];
-// column C holds the tile's error flag.
+// The top-k ids of token t; slots past k, and every slot of a token past T,
+// hold 0x7fffffff (they sort after every real id).  A row of 4n ids (2n)
+// starting on a 16-byte (8-byte) boundary is read 16 (8) bytes at a time:
+// a wave's rows are contiguous, so each instruction covers whole lines
+// instead of one id per lane every 4k bytes.
 template <int KMAX>
-__device__ __forceinline__ void count_tile(const int32_t* __restrict__ idx, int T, int k, int E, FastDiv epr, int C,
+__device__ __forceinline__ void load_ids(const int32_t* __restrict__ idx, int T, int k, int t, int (&ev)[KMAX])
+{
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    typedef int i32x4v __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) ev[j] = 0x7fffffff;
+    if (t < T) {
+        const int32_t* row = idx + (int64_t)t * k;
+        const unsigned long long base = (unsigned long long)idx;
+        if ((k & 3) == 0 && (base & 15) == 0) {  // uniform
+#pragma unroll
+            for (int j = 0; j < KMAX; j += 4)
+                if (j < k) {
+                    const i32x4v v = *(const i32x4v*)(row + j);
+                    ev[j] = v.x;
+                    if (j + 1 < KMAX) ev[j + 1] = v.y;
+                    if (j + 2 < KMAX) ev[j + 2] = v.z;
+                    if (j + 3 < KMAX) ev[j + 3] = v.w;
+                }
+        } else if ((k & 1) == 0 && (base & 7) == 0) {  // uniform
+#pragma unroll
+            for (int j = 0; j < KMAX; j += 2)
+                if (j < k) {
+                    const i32x2 v = *(const i32x2*)(row + j);
+                    ev[j] = v.x;
+                    if (j + 1 < KMAX) ev[j + 1] = v.y;
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j)
+                if (j < k) ev[j] = row[j];
+        }
+    }
+}
+
+// One wave per 64-token tile, its ids already loaded.  hist is column-major
+// [(C+1)][ntiles]; column C holds the tile's error flag.  A tile at or past
+// ntiles (a wave with no tile left in a lock-step loop) only takes part in
+// the barriers.
+template <int KMAX>
+__device__ __forceinline__ void count_tile(const int (&ev)[KMAX], int T, int k, int E, FastDiv epr, int C,
                                            int ntiles, int32_t* __restrict__ hist, int tile, int lane,
                                            unsigned long long* s_mask /* [C], this wave's */)
 {
     const int t = tile * kPlanTile + lane;
-
-    // The ids first (their load overlaps the clearing of the masks).
-    int ev[KMAX];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) ev[j] = -1;
-    if (t < T) {
-        const int32_t* row = idx + (int64_t)t * k;
-#pragma unroll
-        for (int j = 0; j < KMAX; ++j)
-            if (j < k) ev[j] = row[j];
-    }
     for (int i = lane; i < C; i += kWave) s_mask[i] = 0ull;
     __syncthreads();
 
@@ -59,6 +96,7 @@ __device__ __forceinline__ void count_tile(const int32_t* __restrict__ idx, int 
         }
     }
     __syncthreads();
+    if (tile >= ntiles) return;  // uniform
 
     int ecount = 0;
     for (int c = lane; c < C; c += kWave) {
@@ -79,7 +117,10 @@ __global__ __launch_bounds__(kWave) void plan_count_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ hist)
 {
     extern __shared__ unsigned long long s_mask[];  // [C]
-    count_tile<KMAX>(idx, T, k, E, epr, C, ntiles, hist, blockIdx.x, threadIdx.x, s_mask);
+    const int tile = blockIdx.x, lane = threadIdx.x;
+    int ev[KMAX];
+    load_ids<KMAX>(idx, T, k, tile * kPlanTile + lane, ev);
+    count_tile<KMAX>(ev, T, k, E, epr, C, ntiles, hist, tile, lane, s_mask);
 }
 
 // ---------------------------------------------------------------- plan_scan
@@ -178,11 +219,13 @@ struct RowWriter {
     }
 };
 
-// ct_src[c]: column totals; tb_src[c * tb_stride]: this tile's base in
-// column c; status_src[0]: the plan status (global arrays, or their copies
-// in LDS when the whole plan runs in one block).
-template <int KMAX>
-__device__ __forceinline__ void place_tile(const PlaceArgs& a, int tile, int lane,
+// ev: this lane's top-k ids (load_ids); ct_src[c]: column totals;
+// tb_src[c * tb_stride]: this tile's base in column c; status_src[0]: the
+// plan status (global arrays, or their copies in LDS when the whole plan
+// runs in one block).  NCOLS * 64 >= C.  A tile at or past ntiles only
+// takes part in the barriers.
+template <int KMAX, int NCOLS = kMaxCols / kWave>
+__device__ __forceinline__ void place_tile(const PlaceArgs& a, int (&ev)[KMAX], int tile, int lane,
                                            unsigned long long* s_mask /* [C] */, int* s_wbase /* [C] */,
                                            const int32_t* ct_src, const int32_t* tb_src, int tb_stride,
                                            const int32_t* status_src)
@@ -190,21 +233,12 @@ __device__ __forceinline__ void place_tile(const PlaceArgs& a, int tile, int lan
     const int C = a.C, E = a.E, R = a.R;
     const int t = tile * kPlanTile + lane;
     const int k = a.k;
-    constexpr int kCols = kMaxCols / kWave;  // histogram columns per lane
+    constexpr int kCols = NCOLS;  // histogram columns per lane
 
-    // Every global load first, so their latencies overlap: the status word,
-    // this lane's top-k ids, and for each column it owns the column total
-    // and this tile's base within the column.
+    // Every load before the first use, so their latencies overlap: the
+    // status word, and for each column this lane owns the column total and
+    // this tile's base within the column.
     const int status = status_src[0];
-    int ev[KMAX];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) ev[j] = 0x7fffffff;
-    if (t < a.T) {
-        const int32_t* row = a.idx + (int64_t)t * k;
-#pragma unroll
-        for (int j = 0; j < KMAX; ++j)
-            if (j < k) ev[j] = row[j];
-    }
     int ct[kCols], tb[kCols];
 #pragma unroll
     for (int i = 0; i < kCols; ++i) {
@@ -341,39 +375,43 @@ template <int KMAX>
 __global__ __launch_bounds__(kWave) void plan_place_kernel(PlaceArgs a)
 {
     extern __shared__ unsigned long long s_dyn[];
-    place_tile<KMAX>(a, blockIdx.x, threadIdx.x, s_dyn, (int*)(s_dyn + a.C), a.col_total,
-                     a.tile_base + blockIdx.x, a.ntiles, a.status);
+    const int tile = blockIdx.x, lane = threadIdx.x;
+    int ev[KMAX];
+    load_ids<KMAX>(a.idx, a.T, a.k, tile * kPlanTile + lane, ev);
+    place_tile<KMAX>(a, ev, tile, lane, s_dyn, (int*)(s_dyn + a.C), a.col_total, a.tile_base + tile, a.ntiles,
+                     a.status);
 }
 
 // ---------------------------------------------------------------- small batches
 //
 // Up to kSmallTiles tiles, the three steps run in one block of one wave per
 // tile, separated by block barriers instead of kernel boundaries, with the
-// tile histograms, the scanned bases, the column totals and the status in
-// LDS: one launch instead of three and no global round trip between the
-// steps, which is most of the plan's time on a small batch.  The count and
-// place steps are the functions above; the scan is one wave per column.
-// The scan results also go to the workspace for the later kernels.
-#ifndef MS_PLAN_SMALL_TILES
-#define MS_PLAN_SMALL_TILES 16
-#endif
-constexpr int kSmallTiles = MS_PLAN_SMALL_TILES;
-static_assert(kSmallTiles <= 16, "the small plan runs one block of at most 16 waves");
+// tile histograms (scanned in place into the tile bases), the column totals
+// and the status in LDS: one launch instead of three and no global round
+// trip between the steps, which is most of the plan's time on a small
+// batch.  Each lane loads its token's ids once, for both the count and the
+// place step.  The count and place steps are the functions above; the scan
+// is one wave per column.  The scan results also go to the workspace for the
+// later kernels.  (One block is one CU: a block that loops its waves over
+// more tiles measured slower than three launches from 17 tiles on, the
+// CU's memory pipeline taking every tile's scattered index stores.)
+constexpr int kSmallTiles = 16;
 constexpr size_t kSmallLds = 48 * 1024;
 constexpr int kSmallMaxTopK = 16;  // wider rows keep the three launches (registers at 16 waves per block)
+constexpr int kSmallMaxSlots = 32; // tiles x top-k: one CU takes every index store, slower than three launches beyond
 
 // LDS of the one-block plan: per wave its masks and row bases, then the
-// shared histograms, bases, totals and status.
+// shared histograms (plus the error column), the totals and the status.
 static size_t small_plan_lds(int ntiles, int C)
 {
     return (size_t)ntiles * C * (sizeof(unsigned long long) + sizeof(int)) +
-           sizeof(int) * ((size_t)(C + 1) * ntiles + (size_t)C * ntiles + C + 1);
+           sizeof(int) * ((size_t)(C + 1) * ntiles + C + 1);
 }
 
 template <int KMAX>
-__global__ __launch_bounds__(16 * kWave) void plan_small_kernel(PlaceArgs a, int32_t* __restrict__ tile_base,
-                                                                int32_t* __restrict__ col_total,
-                                                                int32_t* __restrict__ status)
+__global__ __launch_bounds__(kSmallTiles * kWave) void plan_small_kernel(PlaceArgs a, int32_t* __restrict__ tile_base,
+                                                                         int32_t* __restrict__ col_total,
+                                                                         int32_t* __restrict__ status)
 {
     extern __shared__ unsigned long long s_dyn[];
     const int C = a.C, ntiles = a.ntiles;
@@ -381,16 +419,20 @@ __global__ __launch_bounds__(16 * kWave) void plan_small_kernel(PlaceArgs a, int
     unsigned long long* s_mask = s_dyn + (size_t)wave * C;
     int* s_ints = (int*)(s_dyn + (size_t)ntiles * C);
     int* s_wbase = s_ints + (size_t)wave * C;
-    int* s_hist = s_ints + (size_t)ntiles * C;      // [(C+1)][ntiles]
-    int* s_tb = s_hist + (size_t)(C + 1) * ntiles;  // [C][ntiles]
-    int* s_ct = s_tb + (size_t)C * ntiles;          // [C]
-    int* s_status = s_ct + C;                       // [1]
-    count_tile<KMAX>(a.idx, a.T, a.k, a.E, a.epr, C, ntiles, s_hist, wave, lane, s_mask);
+    int* s_tb = s_ints + (size_t)ntiles * C;      // [(C+1)][ntiles]: histograms, then tile bases
+    int* s_ct = s_tb + (size_t)(C + 1) * ntiles;  // [C]
+    int* s_status = s_ct + C;                     // [1]
+
+    int ev[KMAX];
+    load_ids<KMAX>(a.idx, a.T, a.k, wave * kPlanTile + lane, ev);
+    count_tile<KMAX>(ev, a.T, a.k, a.E, a.epr, C, ntiles, s_tb, wave, lane, s_mask);
     __syncthreads();  // every tile's histogram is in LDS
+
     // Exclusive scan of each column over the tiles (ntiles <= 64: one lane
-    // per tile); column C holds the error flags.
+    // per tile), in place; column C holds the error flags.
     for (int c = wave; c <= C; c += ntiles) {
-        const int v = lane < ntiles ? s_hist[c * ntiles + lane] : 0;
+        int* col = s_tb + (size_t)c * ntiles;
+        const int v = lane < ntiles ? col[lane] : 0;
         if (c == C) {
             const bool bad = __ballot(v != 0) != 0ull;
             const int st = bad ? MOE_SHUFFLE_E_BAD_INDEX : MOE_SHUFFLE_OK;
@@ -401,7 +443,7 @@ __global__ __launch_bounds__(16 * kWave) void plan_small_kernel(PlaceArgs a, int
         } else {
             const int incl = wave_inclusive_scan(v);
             if (lane < ntiles) {
-                s_tb[c * ntiles + lane] = incl - v;
+                col[lane] = incl - v;
                 tile_base[(int64_t)c * ntiles + lane] = incl - v;
             }
             if (lane == kWave - 1) {
@@ -411,7 +453,91 @@ __global__ __launch_bounds__(16 * kWave) void plan_small_kernel(PlaceArgs a, int
         }
     }
     __syncthreads();  // offsets and status are in LDS
-    place_tile<KMAX>(a, wave, lane, s_mask, s_wbase, s_ct, s_tb + wave, ntiles, s_status);
+    place_tile<KMAX>(a, ev, wave, lane, s_mask, s_wbase, s_ct, s_tb + wave, ntiles, s_status);
+}
+
+// ---------------------------------------------------------------- small batches, narrow histograms
+//
+// Up to 16 tiles with at most 64 histogram columns (E + R <= 64): one launch
+// of one block per tile.  Every block counts every tile again -- wave w
+// counts tile w, a lane's columns fit one 64-bit mask, and a column's count
+// over a tile is the popcount of one ballot -- which gives it the column
+// totals and its own tile's bases without waiting on any other block.  Then
+// the wave that counted the block's tile places it with the functions above
+// (the other waves pass through the same barriers with a tile past the end).
+// Block 0 publishes the status and the column totals, block b column b of
+// the tile bases.  The recount grows with the tiles, the columns and top-k,
+// so larger batches take the other forms.
+constexpr int kRecountMaxCols = kWave;  // one lane per column
+constexpr int kRecountMaxTiles = 16;    // one tile per wave
+constexpr int kRecountMaxWork = 64;     // E + R + 3k: the recount measured faster than the other forms up to here
+
+template <int KMAX>
+__global__ __launch_bounds__(kRecountMaxTiles * kWave) void plan_recount_kernel(PlaceArgs a,
+                                                                               int32_t* __restrict__ tile_base,
+                                                                               int32_t* __restrict__ col_total,
+                                                                               int32_t* __restrict__ status)
+{
+    __shared__ unsigned long long s_mask[kRecountMaxTiles][kRecountMaxCols];
+    __shared__ int s_wbase[kRecountMaxTiles][kRecountMaxCols];
+    __shared__ int s_ct[kRecountMaxCols], s_pre[kRecountMaxCols], s_bad, s_status;
+    const int C = a.C, E = a.E, T = a.T, k = a.k, ntiles = a.ntiles;  // blockDim.x = 64 * ntiles
+    const int wave = wave_id(), lane = lane_id();
+    const int b = blockIdx.x;  // this block's tile
+    const int t = wave * kPlanTile + lane;
+
+    int ev[KMAX];
+    load_ids<KMAX>(a.idx, T, k, t, ev);
+    if (threadIdx.x < C) {
+        s_ct[threadIdx.x] = 0;
+        s_pre[threadIdx.x] = 0;
+    }
+    if (threadIdx.x == 0) s_bad = 0;
+    __syncthreads();
+
+    // Wave w counts tile w: the column totals, and the counts of the tiles
+    // before b.
+    unsigned long long m = 0ull;
+    int bad = 0;
+    if (t < T) {
+        int nslots = 0;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (j < k) {
+                const int e = ev[j];
+                if ((unsigned)e >= (unsigned)E) {
+                    bad = 1;
+                } else {
+                    ++nslots;
+                    m |= 1ull << e;
+                    m |= 1ull << (E + fdiv(e, a.epr));
+                }
+            }
+        // a repeated expert sets its bit once: fewer expert bits than slots
+        if (__popcll(m & ((1ull << E) - 1)) != nslots) bad = 1;  // E < C <= 64
+    }
+    int cnt = 0;
+    for (int c = 0; c < C; ++c) {
+        const int n = __popcll(__ballot((m >> c) & 1ull));
+        cnt = lane == c ? n : cnt;
+    }
+    if (lane < C) {
+        atomicAdd(&s_ct[lane], cnt);
+        if (wave < b) atomicAdd(&s_pre[lane], cnt);
+    }
+    if (__ballot(bad) != 0ull && lane == 0) atomicOr(&s_bad, 1);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        s_status = s_bad ? MOE_SHUFFLE_E_BAD_INDEX : MOE_SHUFFLE_OK;
+        if (b == 0) status[0] = s_status;
+    }
+    if (threadIdx.x < C) {
+        tile_base[(int64_t)threadIdx.x * ntiles + b] = s_pre[threadIdx.x];
+        if (b == 0) col_total[threadIdx.x] = s_ct[threadIdx.x];
+    }
+    __syncthreads();
+    place_tile<KMAX, 1>(a, ev, wave == b ? b : ntiles, lane, s_mask[wave], s_wbase[wave], s_ct, s_pre, 1,
+                        &s_status);
 }
 
 static PlaceArgs place_args(const Layout& L, const PlanPtrs& P, FastDiv epr)
@@ -437,8 +563,18 @@ hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)
     const int ntiles = L.ntiles;
     const size_t lds_count = sizeof(unsigned long long) * L.C;
     const FastDiv epr = make_fastdiv(L.Epr);
+    if (ntiles <= kRecountMaxTiles && L.C <= kRecountMaxCols && L.k <= 16 && L.C + 3 * L.k <= kRecountMaxWork) {
+        const PlaceArgs a = place_args(L, P, epr);
+        const dim3 grid(ntiles), block(ntiles * kWave);
+        if (L.k <= 8)
+            hipLaunchKernelGGL(plan_recount_kernel<8>, grid, block, 0, s, a, P.tile_base, P.col_total, P.status);
+        else
+            hipLaunchKernelGGL(plan_recount_kernel<16>, grid, block, 0, s, a, P.tile_base, P.col_total, P.status);
+        return hipGetLastError();
+    }
     const size_t lds_small = small_plan_lds(ntiles, L.C);
-    if (ntiles <= kSmallTiles && lds_small <= kSmallLds && L.k <= kSmallMaxTopK) {
+    if (ntiles <= kSmallTiles && lds_small <= kSmallLds && L.k <= kSmallMaxTopK &&
+        ntiles * L.k <= kSmallMaxSlots) {
         const PlaceArgs a = place_args(L, P, epr);
         const dim3 grid(1), block(ntiles * kWave);
         if (L.k <= 8)
@@ -463,11 +599,11 @@ hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)
                            epr, L.C, ntiles, P.tile_hist);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    const PlaceArgs a = place_args(L, P, epr);
     hipLaunchKernelGGL(plan_scan_kernel, dim3(L.C + 1), dim3(kBlock), 0, s, P.tile_hist, ntiles, L.C,
                        P.tile_base, P.col_total, P.status);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const PlaceArgs a = place_args(L, P, epr);
     const size_t lds_place = lds_count + sizeof(int) * L.C;
     if (L.k <= 8)
         hipLaunchKernelGGL(plan_place_kernel<8>, dim3(ntiles), dim3(kWave), lds_place, s, a);

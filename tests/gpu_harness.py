@@ -32,12 +32,18 @@ def to_host16(t: torch.Tensor) -> np.ndarray:
 
 
 def run_hip(idx: np.ndarray, x: np.ndarray, w: np.ndarray, H: int, E: int, R: int, ye: np.ndarray | None = None,
-            query_first: bool = True):
-    """plan -> (query) -> dispatch -> combine(ye or xe).  Returns host copies."""
+            query_first: bool = True, idx_shift: int = 0):
+    """plan -> (query) -> dispatch -> combine(ye or xe).  Returns host copies.
+    idx_shift > 0 places the ids that many int32 past a 256-byte boundary."""
     T, k = idx.shape
     dims = ms.dims_of(T, H, E, k, R)
     ws = torch.empty(ms.moe_shuffle_workspace_size(dims), dtype=torch.uint8, device="cuda")
     idx_d = torch.from_numpy(np.ascontiguousarray(idx)).cuda()
+    if idx_shift:
+        buf = torch.empty(T * k + idx_shift, dtype=torch.int32, device="cuda")
+        buf[idx_shift:].copy_(idx_d.view(-1))
+        idx_d = buf[idx_shift:]
+        assert idx_d.data_ptr() % 256 == 4 * idx_shift
     plan = ms.moe_shuffle_plan(dims, idx_d, ws)
     info = ms.moe_shuffle_plan_query(plan) if query_first else None
     KR = min(k, R)
@@ -74,7 +80,7 @@ def compare_plan(g: dict, o: dict):
         np.testing.assert_array_equal(g[key], o[key], err_msg=f"plan array {key}")
 
 
-def check_case(idx, x, w, H, E, R, ye=None, name="", query_first=True):
+def check_case(idx, x, w, H, E, R, ye=None, name="", query_first=True, idx_shift=0):
     """Full parity of one case: plan and dispatch bit-exact, combine <= 1 ulp
     (0 expected), rank rows past N untouched.  query_first=False launches the
     fan-out on the host-side bound T*min(k,R) without a sync, as the bench
@@ -82,7 +88,7 @@ def check_case(idx, x, w, H, E, R, ye=None, name="", query_first=True):
     T, k = idx.shape
     orc = oracle.get()
     say(f"[case] {name} T={T} H={H} E={E} k={k} R={R} query_first={query_first}")
-    g = run_hip(idx, x, w, H, E, R, ye, query_first=query_first)
+    g = run_hip(idx, x, w, H, E, R, ye, query_first=query_first, idx_shift=idx_shift)
     assert g["status"] == 0
     rc, o = orc.plan(idx, H, E, R)
     assert rc == 0

@@ -26,19 +26,25 @@ def _setup(idx, H=64, E=8, R=4):
     return ms, h, torch, dims, ws, plan
 
 
-# Bad rows for both forms of the plan: the one-launch form (at most 16
-# tiles of 64 tokens, top-k <= 16) and the three-launch form (count, scan,
-# place), whose status travels from the count kernel's error column through
-# the scan to the place kernel's early exit.
+# Bad rows for every form of the plan: recount (one block per tile, each
+# counting every tile again), one block of one wave per tile, and three
+# launches (count, scan, place), where the status travels from the count
+# kernel's error column through the scan to the place kernel's early exit.
 BAD_CASES = [
     # name, T, E, k, R, rows made bad
-    ("one-launch", 300, 8, 2, 4, (137,)),
-    ("one-launch-last-tile", 1024, 8, 2, 4, (1023,)),       # 16 tiles, the bad row in the last
-    ("three-launch-tiles", 1100, 8, 2, 4, (1050,)),          # 18 tiles, the bad row in tile 16
-    ("three-launch-last-tile", 4096, 8, 2, 4, (4095,)),      # 64 tiles, the bad row in the last
-    ("three-launch-mid-size", 4200, 8, 2, 4, (4150,)),       # 66 tiles, the bad row in tile 64
-    ("three-launch-topk-first", 500, 32, 17, 4, (3,)),       # top-17, the bad row in tile 0
-    ("three-launch-topk-last", 500, 32, 17, 4, (499,)),      # ... and in the last, ragged tile
+    ("recount", 300, 8, 2, 4, (137,)),
+    ("recount-last-tile", 1024, 8, 2, 4, (1023,)),             # 16 tiles, the bad row in the last
+    ("recount-first-tile", 1024, 8, 2, 4, (0,)),               # ... and in tile 0
+    ("recount-topk12", 500, 12, 12, 4, (499,)),                # 16 ids per lane
+    ("one-block", 300, 56, 2, 8, (137,)),                      # 64 columns, 64 + 6 > 64
+    ("one-block-last-tile", 512, 56, 4, 8, (511,)),            # 8 tiles x top-4
+    ("three-launch", 1100, 8, 2, 4, (1050,)),                  # 18 tiles, the bad row in tile 16
+    ("three-launch-last-tile", 4096, 8, 2, 4, (4095,)),        # 64 tiles, the bad row in the last
+    ("three-launch-first-tile", 4096, 8, 2, 4, (0,)),          # ... and in tile 0
+    ("three-launch-topk17-first", 500, 32, 17, 4, (3,)),       # top-17, the bad row in tile 0
+    ("three-launch-topk17-last", 500, 32, 17, 4, (499,)),      # ... and in the last, ragged tile
+    ("three-launch-mid-size", 4200, 8, 2, 4, (4150,)),         # 66 tiles, the bad row in tile 64
+    ("three-launch-wide", 1100, 960, 2, 64, (5,)),             # 18 tiles x 1024 columns
 ]
 
 WS_FILL = 0x5A  # workspace bytes before the plan: index arrays must keep them

@@ -76,17 +76,30 @@ def test_ragged_and_edge_shapes(T, H, E, k, R):
     harness().check_case(idx, x, w, H, E, R, ye=ye, name=f"ragged-{T}x{H}")
 
 
-# Either side of the limits of the one-launch plan (at most 16 tiles of 64
-# tokens, 48 KiB of LDS, top-k <= 16): both plan forms must give the
-# oracle's arrays bit for bit.
+# Either side of the limits of the three plan forms, which must all give
+# the oracle's arrays bit for bit:
+# - recount: one block per tile, each block counting every tile again; at
+#   most 16 tiles of 64 tokens, E + R <= 64, top-k <= 16, E + R + 3k <= 64;
+# - one block, one wave per tile: at most 16 tiles, 48 KiB of LDS, top-k
+#   <= 16, tiles x top-k <= 32;
+# - three launches (count, scan, place): everything else.
 PLAN_FORMS = [
     # T, H, E, k, R
-    (1024, 64, 32, 8, 8),       # 16 tiles: one launch
+    (1024, 64, 32, 8, 8),       # 16 tiles x 40 columns, 40 + 24 = 64: recount
+    (1024, 64, 32, 9, 8),       # 40 + 27 > 64, 144 slots: three launches
+    (500, 64, 12, 12, 4),       # top-12, 16 + 36 <= 64: recount with 16 ids per lane
     (1025, 64, 32, 8, 8),       # 17 tiles: three launches
-    (128, 64, 1024 - 64, 8, 64),  # 2 tiles x 1024 columns, 44 KiB of LDS: one launch
-    (129, 64, 1024 - 64, 8, 64),  # 3 tiles, 64 KiB: three launches
-    (500, 64, 64, 16, 8),       # top-16: one launch
+    (256, 64, 56, 2, 8),        # 4 tiles x 64 columns, 64 + 6 > 64: one block
+    (512, 64, 56, 4, 8),        # 8 tiles x top-4 = 32 slots: one block
+    (576, 64, 56, 4, 8),        # 9 tiles x top-4 = 36 slots: three launches
+    (500, 64, 16, 16, 4),       # top-16, 8 x 16 slots: three launches
+    (2000, 64, 32, 8, 8),       # 32 tiles, ragged last tile: three launches
+    (4096, 64, 8, 2, 8),        # 64 tiles (the Mixtral-like shape): three launches
+    (4096, 64, 56, 8, 8),       # 64 tiles x 64 columns: three launches
+    (128, 64, 1024 - 64, 8, 64),  # 2 tiles x 1024 columns, 36 KiB of LDS: one block
+    (129, 64, 1024 - 64, 8, 64),  # 3 tiles, 52 KiB: three launches
     (500, 64, 64, 17, 8),       # top-17: three launches
+    (4200, 64, 32, 17, 8),      # top-17, 66 tiles: three launches
 ]
 
 
@@ -98,9 +111,30 @@ def test_both_plan_forms(T, H, E, k, R):
     harness().check_case(idx, x, w, H, E, R, name=f"plan-form-{T}-{E}-{k}")
 
 
+# The plan reads a row of 4n (2n) ids 16 (8) bytes at a time when the ids
+# start on such a boundary, else one id at a time: ids placed 4 and 8 bytes
+# past a boundary, through every plan form, give the oracle's arrays too.
+ID_ALIGN = [
+    # T, E, k, R, shift in int32
+    (300, 16, 8, 4, 1), (300, 16, 8, 4, 2), (300, 16, 2, 4, 1),       # recount
+    (300, 56, 4, 8, 1), (300, 56, 2, 8, 1),                           # one block
+    (3000, 16, 8, 4, 1), (3000, 16, 8, 4, 2), (3000, 16, 2, 4, 1),    # three launches
+    (5000, 64, 8, 8, 1), (5000, 64, 12, 8, 2), (5000, 64, 2, 8, 1),   # three launches
+]
+
+
+@pytest.mark.parametrize("T,E,k,R,shift", ID_ALIGN)
+def test_ids_off_the_vector_boundary(T, E, k, R, shift):
+    rng = np.random.default_rng(T * 3 + E + k * 5 + shift)
+    idx, w = synth.random_routing(rng, T, E, k, signed_gates=True)
+    x = synth.random_bf16(rng, (T, 64))
+    harness().check_case(idx, x, w, 64, E, R, name=f"id-align-{T}-{E}-{k}+{shift}", idx_shift=shift)
+
+
 def _plan_form_shapes(n=40, seed=91):
-    """Seeded shapes around the one-launch plan's limits: up to 18 tiles,
-    top-k up to 20, histograms up to 1024 columns."""
+    """Seeded shapes around the plan forms' limits: up to 18 tiles, top-k up
+    to 20, histograms up to 1024 columns; then 16 to 66 tiles at top-k up to
+    10 and up to 160 columns."""
     rng = np.random.default_rng(seed)
     shapes = []
     while len(shapes) < n:
@@ -110,6 +144,13 @@ def _plan_form_shapes(n=40, seed=91):
             continue
         k = int(rng.integers(1, min(E, 20) + 1))
         shapes.append((int(rng.integers(0, 18 * 64 + 1)), 8 * int(rng.integers(1, 40)), E, k, R))
+    while len(shapes) < n + n // 2:
+        R = int(rng.choice([1, 2, 4, 8, 16]))
+        E = R * int(rng.integers(1, 9))
+        if E + R > 160:
+            continue
+        k = int(rng.integers(1, min(E, 10) + 1))
+        shapes.append((int(rng.integers(16 * 64, 66 * 64 + 1)), 8 * int(rng.integers(1, 20)), E, k, R))
     return shapes
 
 

@@ -428,8 +428,8 @@ __global__ __launch_bounds__(kSmallTiles * kWave) void plan_small_kernel(PlaceAr
     count_tile<KMAX>(ev, a.T, a.k, a.E, a.epr, C, ntiles, s_tb, wave, lane, s_mask);
     __syncthreads();  // every tile's histogram is in LDS
 
-    // Exclusive scan of each column over the tiles (ntiles <= 64: one lane
-    // per tile), in place; column C holds the error flags.
+    // Exclusive scan of each column over the tiles (at most 16: one lane per
+    // tile), in place; column C holds the error flags.
     for (int c = wave; c <= C; c += ntiles) {
         int* col = s_tb + (size_t)c * ntiles;
         const int v = lane < ntiles ? col[lane] : 0;

@@ -76,6 +76,8 @@ def test_pipelined_ranges_match_oracle(cfg_id, chunks):
     (300, 96, 12, 3, 1, [0, 300]),
     (1000, 1032, 32, 4, 8, [0, 64, 192, 640, 1000]),   # ranges on the 64-token plan tile
     (130, 64, 16, 4, 4, [0, 64, 128, 130]),
+    (300, 64, 56, 2, 8, [0, 128, 300]),                 # a plan made in one block (64 columns)
+    (1000, 64, 8, 2, 4, [0, 448, 1000]),                # a plan made one block per tile (recount)
 ])
 def test_ragged_ranges(T, H, E, k, R, bounds):
     import gpu_harness as h

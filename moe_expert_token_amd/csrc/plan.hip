@@ -11,10 +11,11 @@
 //               offsets, and gives every (token, rank) and (token, expert)
 //               pair its row: tile base + mbcnt(mask).  Rows come out in
 //               ascending token order inside every segment.
-//   plan_recount  up to 16 tiles with E + R <= 64: one launch of one
-//               block per tile, each block counting every tile again
-//               (ballots over per-lane column masks), so no block waits on
-//               another; then one wave places the block's tile.
+//   plan_recount  up to 48 tiles with E + R <= 64 (while the recount
+//               stays small): one launch of one block per tile, each block
+//               counting every tile again (ballots over per-lane column
+//               masks), so no block waits on another; then one wave places
+//               the block's tile.
 //   plan_small  up to 16 tiles (and 32 tile-slots): the three steps in one
 //               block of one wave per tile.
 // Each form loads a token's ids once, for both its count and place steps.
@@ -66,9 +67,7 @@ __device__ __forceinline__ void load_ids(const int32_t* __restrict__ idx, int T,
 }
 
 // One wave per 64-token tile, its ids already loaded.  hist is column-major
-// [(C+1)][ntiles]; column C holds the tile's error flag.  A tile at or past
-// ntiles (a wave with no tile left in a lock-step loop) only takes part in
-// the barriers.
+// [(C+1)][ntiles]; column C holds the tile's error flag.
 template <int KMAX>
 __device__ __forceinline__ void count_tile(const int (&ev)[KMAX], int T, int k, int E, FastDiv epr, int C,
                                            int ntiles, int32_t* __restrict__ hist, int tile, int lane,
@@ -96,7 +95,6 @@ __device__ __forceinline__ void count_tile(const int (&ev)[KMAX], int T, int k, 
         }
     }
     __syncthreads();
-    if (tile >= ntiles) return;  // uniform
 
     int ecount = 0;
     for (int c = lane; c < C; c += kWave) {
@@ -458,36 +456,42 @@ __global__ __launch_bounds__(kSmallTiles * kWave) void plan_small_kernel(PlaceAr
 
 // ---------------------------------------------------------------- small batches, narrow histograms
 //
-// Up to 16 tiles with at most 64 histogram columns (E + R <= 64): one launch
-// of one block per tile.  Every block counts every tile again -- wave w
-// counts tile w, a lane's columns fit one 64-bit mask, and a column's count
-// over a tile is the popcount of one ballot -- which gives it the column
-// totals and its own tile's bases without waiting on any other block.  Then
-// the wave that counted the block's tile places it with the functions above
-// (the other waves pass through the same barriers with a tile past the end).
-// Block 0 publishes the status and the column totals, block b column b of
-// the tile bases.  The recount grows with the tiles, the columns and top-k,
-// so larger batches take the other forms.
+// Up to 48 tiles with at most 64 histogram columns (E + R <= 64): one launch
+// of one block per tile.  Every block counts every tile again -- wave w of
+// the min(tiles, 16) waves counts tiles w, w + 16, w + 32 (the same number
+// of trips in every wave), a lane's columns fit one 64-bit mask, and a
+// column's count over a tile is the popcount of one ballot -- which gives it
+// the column totals and its own tile's bases without waiting on any other
+// block.  Then the wave that counted the block's tile places it with the
+// functions above, from the ids it holds (the other waves pass through the
+// same barriers with a tile past the end).  Block 0 publishes the status and
+// the column totals, block b column b of the tile bases.  The recount grows
+// with trips x (E + R + 3k) (ballots per column, id work per slot), so it is
+// used only while that stays small; larger batches take the other forms.
 constexpr int kRecountMaxCols = kWave;  // one lane per column
-constexpr int kRecountMaxTiles = 16;    // one tile per wave
-constexpr int kRecountMaxWork = 64;     // E + R + 3k: the recount measured faster than the other forms up to here
+constexpr int kRecountWaves = 16;
+constexpr int kRecountMaxTrips = 3;     // tiles per wave
+constexpr int kRecountMaxTiles = kRecountWaves * kRecountMaxTrips;
+constexpr int kRecountMaxWork = 66;     // trips x (E + R + 3k): measured faster than the other forms up to here
 
-template <int KMAX>
-__global__ __launch_bounds__(kRecountMaxTiles * kWave) void plan_recount_kernel(PlaceArgs a,
-                                                                               int32_t* __restrict__ tile_base,
-                                                                               int32_t* __restrict__ col_total,
-                                                                               int32_t* __restrict__ status)
+template <int KMAX, int TRIPS>
+__global__ __launch_bounds__(kRecountWaves * kWave) void plan_recount_kernel(PlaceArgs a,
+                                                                            int32_t* __restrict__ tile_base,
+                                                                            int32_t* __restrict__ col_total,
+                                                                            int32_t* __restrict__ status)
 {
-    __shared__ unsigned long long s_mask[kRecountMaxTiles][kRecountMaxCols];
-    __shared__ int s_wbase[kRecountMaxTiles][kRecountMaxCols];
+    __shared__ unsigned long long s_mask[kRecountWaves][kRecountMaxCols];
+    __shared__ int s_wbase[kRecountWaves][kRecountMaxCols];
     __shared__ int s_ct[kRecountMaxCols], s_pre[kRecountMaxCols], s_bad, s_status;
-    const int C = a.C, E = a.E, T = a.T, k = a.k, ntiles = a.ntiles;  // blockDim.x = 64 * ntiles
+    const int C = a.C, E = a.E, T = a.T, k = a.k, ntiles = a.ntiles;
+    const int nwaves = blockDim.x / kWave;             // min(ntiles, 16)
+    const int trips = (ntiles + nwaves - 1) / nwaves;  // <= TRIPS
     const int wave = wave_id(), lane = lane_id();
     const int b = blockIdx.x;  // this block's tile
-    const int t = wave * kPlanTile + lane;
 
-    int ev[KMAX];
-    load_ids<KMAX>(a.idx, T, k, t, ev);
+    int ev[TRIPS][KMAX];
+#pragma unroll
+    for (int it = 0; it < TRIPS; ++it) load_ids<KMAX>(a.idx, T, k, (wave + it * nwaves) * kPlanTile + lane, ev[it]);
     if (threadIdx.x < C) {
         s_ct[threadIdx.x] = 0;
         s_pre[threadIdx.x] = 0;
@@ -495,37 +499,43 @@ __global__ __launch_bounds__(kRecountMaxTiles * kWave) void plan_recount_kernel(
     if (threadIdx.x == 0) s_bad = 0;
     __syncthreads();
 
-    // Wave w counts tile w: the column totals, and the counts of the tiles
-    // before b.
-    unsigned long long m = 0ull;
-    int bad = 0;
-    if (t < T) {
-        int nslots = 0;
+    // The column totals, and the counts of the tiles before b.
+    const unsigned long long emask = (1ull << E) - 1;  // E < C <= 64
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j)
-            if (j < k) {
-                const int e = ev[j];
-                if ((unsigned)e >= (unsigned)E) {
-                    bad = 1;
-                } else {
-                    ++nslots;
-                    m |= 1ull << e;
-                    m |= 1ull << (E + fdiv(e, a.epr));
+    for (int it = 0; it < TRIPS; ++it) {
+        if (it >= trips) break;  // uniform
+        const int tile = wave + it * nwaves;
+        const int t = tile * kPlanTile + lane;
+        unsigned long long m = 0ull;
+        int bad = 0;
+        if (t < T) {
+            int nslots = 0;
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j)
+                if (j < k) {
+                    const int e = ev[it][j];
+                    if ((unsigned)e >= (unsigned)E) {
+                        bad = 1;
+                    } else {
+                        ++nslots;
+                        m |= 1ull << e;
+                        m |= 1ull << (E + fdiv(e, a.epr));
+                    }
                 }
-            }
-        // a repeated expert sets its bit once: fewer expert bits than slots
-        if (__popcll(m & ((1ull << E) - 1)) != nslots) bad = 1;  // E < C <= 64
+            // a repeated expert sets its bit once: fewer expert bits than slots
+            if (__popcll(m & emask) != nslots) bad = 1;
+        }
+        int cnt = 0;
+        for (int c = 0; c < C; ++c) {
+            const int n = __popcll(__ballot((m >> c) & 1ull));
+            cnt = lane == c ? n : cnt;
+        }
+        if (lane < C) {
+            atomicAdd(&s_ct[lane], cnt);
+            if (tile < b) atomicAdd(&s_pre[lane], cnt);
+        }
+        if (__ballot(bad) != 0ull && lane == 0) atomicOr(&s_bad, 1);
     }
-    int cnt = 0;
-    for (int c = 0; c < C; ++c) {
-        const int n = __popcll(__ballot((m >> c) & 1ull));
-        cnt = lane == c ? n : cnt;
-    }
-    if (lane < C) {
-        atomicAdd(&s_ct[lane], cnt);
-        if (wave < b) atomicAdd(&s_pre[lane], cnt);
-    }
-    if (__ballot(bad) != 0ull && lane == 0) atomicOr(&s_bad, 1);
     __syncthreads();
     if (threadIdx.x == 0) {
         s_status = s_bad ? MOE_SHUFFLE_E_BAD_INDEX : MOE_SHUFFLE_OK;
@@ -536,7 +546,16 @@ __global__ __launch_bounds__(kRecountMaxTiles * kWave) void plan_recount_kernel(
         if (b == 0) col_total[threadIdx.x] = s_ct[threadIdx.x];
     }
     __syncthreads();
-    place_tile<KMAX, 1>(a, ev, wave == b ? b : ntiles, lane, s_mask[wave], s_wbase[wave], s_ct, s_pre, 1,
+
+    // The wave that counted tile b places it.
+    const int owner = b % nwaves, it_b = b / nwaves;
+    int evb[KMAX];
+#pragma unroll
+    for (int it = 0; it < TRIPS; ++it)
+        if (it == it_b)  // uniform
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) evb[j] = ev[it][j];
+    place_tile<KMAX, 1>(a, evb, wave == owner ? b : ntiles, lane, s_mask[wave], s_wbase[wave], s_ct, s_pre, 1,
                         &s_status);
 }
 
@@ -563,13 +582,20 @@ hipError_t launch_plan(const Layout& L, const PlanPtrs& P, hipStream_t s)
     const int ntiles = L.ntiles;
     const size_t lds_count = sizeof(unsigned long long) * L.C;
     const FastDiv epr = make_fastdiv(L.Epr);
-    if (ntiles <= kRecountMaxTiles && L.C <= kRecountMaxCols && L.k <= 16 && L.C + 3 * L.k <= kRecountMaxWork) {
+    const int rwaves = ntiles < kRecountWaves ? ntiles : kRecountWaves;
+    const int rtrips = (ntiles + rwaves - 1) / rwaves;
+    if (ntiles <= kRecountMaxTiles && L.C <= kRecountMaxCols && L.k <= (rtrips == 1 ? 16 : 8) &&
+        rtrips * (L.C + 3 * L.k) <= kRecountMaxWork) {
         const PlaceArgs a = place_args(L, P, epr);
-        const dim3 grid(ntiles), block(ntiles * kWave);
-        if (L.k <= 8)
-            hipLaunchKernelGGL(plan_recount_kernel<8>, grid, block, 0, s, a, P.tile_base, P.col_total, P.status);
+        const dim3 grid(ntiles), block(rwaves * kWave);
+        if (rtrips == 1 && L.k <= 8)
+            hipLaunchKernelGGL((plan_recount_kernel<8, 1>), grid, block, 0, s, a, P.tile_base, P.col_total, P.status);
+        else if (rtrips == 1)
+            hipLaunchKernelGGL((plan_recount_kernel<16, 1>), grid, block, 0, s, a, P.tile_base, P.col_total,
+                               P.status);
         else
-            hipLaunchKernelGGL(plan_recount_kernel<16>, grid, block, 0, s, a, P.tile_base, P.col_total, P.status);
+            hipLaunchKernelGGL((plan_recount_kernel<8, kRecountMaxTrips>), grid, block, 0, s, a, P.tile_base,
+                               P.col_total, P.status);
         return hipGetLastError();
     }
     const size_t lds_small = small_plan_lds(ntiles, L.C);

@@ -27,18 +27,21 @@ def _setup(idx, H=64, E=8, R=4):
 
 
 # Bad rows for every form of the plan: recount (one block per tile, each
-# counting every tile again), one block of one wave per tile, and three
-# launches (count, scan, place), where the status travels from the count
-# kernel's error column through the scan to the place kernel's early exit.
+# counting every tile again, a wave up to 3 tiles), one block of one wave
+# per tile, and three launches (count, scan, place), where the status
+# travels from the count kernel's error column through the scan to the
+# place kernel's early exit.
 BAD_CASES = [
     # name, T, E, k, R, rows made bad
     ("recount", 300, 8, 2, 4, (137,)),
     ("recount-last-tile", 1024, 8, 2, 4, (1023,)),             # 16 tiles, the bad row in the last
     ("recount-first-tile", 1024, 8, 2, 4, (0,)),               # ... and in tile 0
     ("recount-topk12", 500, 12, 12, 4, (499,)),                # 16 ids per lane
-    ("one-block", 300, 56, 2, 8, (137,)),                      # 64 columns, 64 + 6 > 64
+    ("one-block", 300, 56, 2, 8, (137,)),                      # 64 columns, 64 + 6 > 66
     ("one-block-last-tile", 512, 56, 4, 8, (511,)),            # 8 tiles x top-4
-    ("three-launch", 1100, 8, 2, 4, (1050,)),                  # 18 tiles, the bad row in tile 16
+    ("recount-second-trip", 1100, 8, 2, 4, (1050,)),           # 18 tiles, the bad row in tile 16 (wave 0's second)
+    ("recount-last-trip", 3072, 8, 2, 4, (3071,)),             # 48 tiles, the bad row in wave 15's third
+    ("three-launch", 1100, 32, 2, 8, (1050,)),                 # 18 tiles x 40 columns, the bad row in tile 16
     ("three-launch-last-tile", 4096, 8, 2, 4, (4095,)),        # 64 tiles, the bad row in the last
     ("three-launch-first-tile", 4096, 8, 2, 4, (0,)),          # ... and in tile 0
     ("three-launch-topk17-first", 500, 32, 17, 4, (3,)),       # top-17, the bad row in tile 0

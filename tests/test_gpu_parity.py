@@ -79,17 +79,24 @@ def test_ragged_and_edge_shapes(T, H, E, k, R):
 # Either side of the limits of the three plan forms, which must all give
 # the oracle's arrays bit for bit:
 # - recount: one block per tile, each block counting every tile again; at
-#   most 16 tiles of 64 tokens, E + R <= 64, top-k <= 16, E + R + 3k <= 64;
+#   most 48 tiles of 64 tokens (up to 3 per wave of 16), E + R <= 64, top-k
+#   <= 16 up to 16 tiles and <= 8 above, trips x (E + R + 3k) <= 66;
 # - one block, one wave per tile: at most 16 tiles, 48 KiB of LDS, top-k
 #   <= 16, tiles x top-k <= 32;
 # - three launches (count, scan, place): everything else.
 PLAN_FORMS = [
     # T, H, E, k, R
     (1024, 64, 32, 8, 8),       # 16 tiles x 40 columns, 40 + 24 = 64: recount
-    (1024, 64, 32, 9, 8),       # 40 + 27 > 64, 144 slots: three launches
-    (500, 64, 12, 12, 4),       # top-12, 16 + 36 <= 64: recount with 16 ids per lane
+    (1024, 64, 32, 9, 8),       # 40 + 27 > 66, 144 slots: three launches
+    (1025, 64, 8, 2, 8),        # 17 tiles x 16 columns, 2 x 22: recount, wave 0 counts tiles 0 and 16
+    (2048, 64, 16, 2, 8),       # 32 tiles, 2 x 30: recount
+    (2048, 64, 20, 2, 10),      # 32 tiles, 2 x 36 > 66: three launches
+    (3000, 64, 8, 2, 8),        # 47 tiles, 3 x 22: recount, waves with 2 and 3 tiles
+    (3072, 64, 8, 2, 8),        # 48 tiles: recount, 3 tiles per wave
+    (3073, 64, 8, 2, 8),        # 49 tiles: three launches
+    (500, 64, 12, 12, 4),       # top-12, 16 + 36 <= 66: recount with 16 ids per lane
     (1025, 64, 32, 8, 8),       # 17 tiles: three launches
-    (256, 64, 56, 2, 8),        # 4 tiles x 64 columns, 64 + 6 > 64: one block
+    (256, 64, 56, 2, 8),        # 4 tiles x 64 columns, 64 + 6 > 66: one block
     (512, 64, 56, 4, 8),        # 8 tiles x top-4 = 32 slots: one block
     (576, 64, 56, 4, 8),        # 9 tiles x top-4 = 36 slots: three launches
     (500, 64, 16, 16, 4),       # top-16, 8 x 16 slots: three launches

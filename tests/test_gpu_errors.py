@@ -41,6 +41,7 @@ BAD_CASES = [
     ("one-block-last-tile", 512, 56, 4, 8, (511,)),            # 8 tiles x top-4
     ("recount-second-trip", 1100, 8, 2, 4, (1050,)),           # 18 tiles, the bad row in tile 16 (wave 0's second)
     ("recount-last-trip", 3072, 8, 2, 4, (3071,)),             # 48 tiles, the bad row in wave 15's third
+    ("recount-trips-topk8", 1100, 8, 8, 1, (1099,)),           # 18 tiles at top-8, the bad row in the last
     ("three-launch", 1100, 32, 2, 8, (1050,)),                 # 18 tiles x 40 columns, the bad row in tile 16
     ("three-launch-last-tile", 4096, 8, 2, 4, (4095,)),        # 64 tiles, the bad row in the last
     ("three-launch-first-tile", 4096, 8, 2, 4, (0,)),          # ... and in tile 0

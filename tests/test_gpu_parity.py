@@ -94,6 +94,8 @@ PLAN_FORMS = [
     (3000, 64, 8, 2, 8),        # 47 tiles, 3 x 22: recount, waves with 2 and 3 tiles
     (3072, 64, 8, 2, 8),        # 48 tiles: recount, 3 tiles per wave
     (3073, 64, 8, 2, 8),        # 49 tiles: three launches
+    (1100, 64, 8, 8, 1),        # 18 tiles at top-8 of 8 experts, 2 x 33: recount, 8 ids per lane in two 16-byte loads
+    (2500, 64, 8, 4, 2),        # 40 tiles at top-4, 3 x 22: recount
     (500, 64, 12, 12, 4),       # top-12, 16 + 36 <= 66: recount with 16 ids per lane
     (1025, 64, 32, 8, 8),       # 17 tiles: three launches
     (256, 64, 56, 2, 8),        # 4 tiles x 64 columns, 64 + 6 > 66: one block

@@ -78,6 +78,7 @@ def test_pipelined_ranges_match_oracle(cfg_id, chunks):
     (130, 64, 16, 4, 4, [0, 64, 128, 130]),
     (300, 64, 56, 2, 8, [0, 128, 300]),                 # a plan made in one block (64 columns)
     (1000, 64, 8, 2, 4, [0, 448, 1000]),                # a plan made one block per tile (recount)
+    (2500, 64, 8, 2, 8, [0, 1088, 2048, 2500]),         # recount with up to 3 tiles per wave
 ])
 def test_ragged_ranges(T, H, E, k, R, bounds):
     import gpu_harness as h
